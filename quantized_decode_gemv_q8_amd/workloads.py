@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs for the Q8_0 matvec and the i8 dot_t.
+
+This module only draws random numbers: it holds none of the method's
+arithmetic, so both the library's tests/bench and the CPU oracle can consume
+its arrays.  numpy ``Generator(PCG64)``; draw order is A, then W, then S.
+
+Shapes and value ranges follow the decode-step projections the "Q8_0 matvec"
+page describes (one activation row against a large i8 weight matrix with one
+f32 scale per 32-row block and column).  The layer shapes stand in for
+attention / MLP projections of 7B- and 70B-class models; no trained weights
+are involved.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+BLOCK = 32  # Q8_0 block length along K
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    op: str          # "q8" or "dot_t"
+    M: int
+    K: int
+    N: int
+    a_dist: str      # "u11" (f32 U[-1,1]), "normal" (f32 N(0,1)), "i8full" (U{-128..127})
+    w_dist: str      # "i8sym" (U{-127..127}) or "i8full" (U{-128..127})
+    seed: tuple      # base seed; copy j uses seed + (j,) unless ``fixed_seed``
+    fixed_seed: bool = False
+
+    @property
+    def KB(self):
+        return (self.K + BLOCK - 1) // BLOCK
+
+    def algorithmic_bytes(self):
+        """Bytes the method must move once each (reads of A, W, S; write of C)."""
+        if self.op == "q8":
+            return self.K * self.N + 4 * self.KB * self.N + 4 * self.M * self.K + 4 * self.M * self.N
+        return self.M * self.K + self.N * self.K + 4 * self.M * self.N
+
+
+WORKLOADS = {
+    # tiny case that the exact brute force and the oracle finish in a blink
+    "tiny": Workload("tiny", "q8", 1, 256, 128, "u11", "i8sym", (0,), fixed_seed=True),
+    # 7B-class attention projection
+    "attn4096": Workload("attn4096", "q8", 1, 4096, 4096, "normal", "i8sym", (2, 0)),
+    # 70B-class MLP up-projection and its transpose (the headline shape)
+    "mlp_up_8192x28672": Workload("mlp_up_8192x28672", "q8", 1, 8192, 28672, "normal", "i8sym", (3, 0)),
+    "mlp_down_28672x8192": Workload("mlp_down_28672x8192", "q8", 1, 28672, 8192, "normal", "i8sym", (3, 1)),
+    # ragged batched case: 4 rows, K=4100 (last block 4 rows), N=5000
+    "ragged_m4": Workload("ragged_m4", "q8", 4, 4100, 5000, "normal", "i8sym", (4, 0)),
+    # integer dot_t, weights stored one output row per row
+    "dot_t_16x4096x4096": Workload("dot_t_16x4096x4096", "dot_t", 16, 4096, 4096, "i8full", "i8full", (5, 0)),
+}
+
+
+def _draw(rng, dist, shape):
+    if dist == "u11":
+        return rng.uniform(-1.0, 1.0, shape).astype(np.float32)
+    if dist == "normal":
+        return rng.standard_normal(shape, dtype=np.float32)
+    if dist == "i8sym":
+        return rng.integers(-127, 128, shape, dtype=np.int8)
+    if dist == "i8full":
+        return rng.integers(-128, 128, shape, dtype=np.int8)
+    if dist == "scale":
+        return rng.uniform(0.001, 0.02, shape).astype(np.float32)
+    raise ValueError(dist)
+
+
+def rng_for(seed):
+    return np.random.default_rng(list(seed) if isinstance(seed, (tuple, list)) else seed)
+
+
+def q8_inputs(M, K, N, seed, a_dist="normal", w_dist="i8sym"):
+    """(A f32 [M,K], W i8 [K,N], S f32 [ceil(K/32),N]) drawn in that order."""
+    rng = rng_for(seed)
+    A = _draw(rng, a_dist, (M, K))
+    W = _draw(rng, w_dist, (K, N))
+    S = _draw(rng, "scale", ((K + BLOCK - 1) // BLOCK, N))
+    return A, W, S
+
+
+def dot_t_inputs(M, K, N, seed, dist="i8full"):
+    """(A i8 [M,K], W i8 [N,K]) drawn in that order."""
+    rng = rng_for(seed)
+    A = _draw(rng, dist, (M, K))
+    W = _draw(rng, dist, (N, K))
+    return A, W
+
+
+def make(name, copy=0):
+    """Inputs of a named workload; copy j of a rotated set uses its own seed."""
+    wl = WORKLOADS[name]
+    seed = wl.seed if wl.fixed_seed else tuple(wl.seed) + (copy,)
+    if wl.op == "q8":
+        if wl.fixed_seed:
+            seed = wl.seed[0]
+        return q8_inputs(wl.M, wl.K, wl.N, seed, wl.a_dist, wl.w_dist)
+    return dot_t_inputs(wl.M, wl.K, wl.N, seed, wl.a_dist)
