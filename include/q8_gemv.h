@@ -1,0 +1,133 @@
+/*
+ * q8_gemv.h -- C ABI of the MI355X (gfx950) Q8_0 matvec and i8 dot_t library.
+ *
+ * Operations (Phobos documentation pages):
+ *   q8_matvec  "Q8_0 matvec" (docs/examples/q8-matvec), section "The tensors":
+ *              C[m,n] = sum_k A[m,k] * W[k,n] * S[k/32, n], with i8 weights,
+ *              one f32 scale per block of 32 rows along K and per column.
+ *              Section "Factoring out the scale": the scale is applied once
+ *              per block and column to the block's unscaled partial.
+ *              Section "Bounds": N and K need not be multiples of any tile;
+ *              the ragged column tile and the K remainder block are masked.
+ *   q8_dot_t   "dot and tensor cores" (docs/language/dot-and-tensor-cores),
+ *              table of built-ins and section "Hardware paths":
+ *              C[m,n] = sum_k A[m,k] * W[n,k], i8 operands, i32 result.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers (memory of the current HIP
+ *     device) to dense row-major arrays; there are no leading-dimension
+ *     arguments.  The caller owns them; the library only reads the inputs
+ *     and overwrites the output (it never reads C).  C must not alias an
+ *     input.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous on that stream: a status of Q8_OK means the work
+ *     was enqueued; faults surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued.  No
+ *     C++ exception crosses this boundary.
+ *   - Sizes: every extent must be >= 0.  M == 0 or N == 0 is a no-op.  The
+ *     library uses 32-bit element offsets, so K*N, M*K and M*N must each be
+ *     below 2^31 (otherwise Q8_ERR_TOO_LARGE).
+ *   - Thread safety: concurrent calls are safe on distinct streams.  The
+ *     split-K workspace of q8_matvec is owned by the library, one per
+ *     (device, stream); it is allocated on the first call that needs it on
+ *     that stream (so that first call must not run under stream capture) and
+ *     freed by q8_release().
+ */
+#ifndef Q8_GEMV_H
+#define Q8_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum q8_status {
+  Q8_OK = 0,
+  Q8_ERR_INVALID = 1,            /* negative extent, null pointer with a non-zero extent, bad plan */
+  Q8_ERR_TOO_LARGE = 2,          /* an offset would not fit the library's 32-bit indexing */
+  Q8_ERR_UNSUPPORTED_DEVICE = 3, /* the current device is not gfx950 */
+  Q8_ERR_HIP = 4                 /* a HIP call failed; see q8_last_hip_error() */
+} q8_status;
+
+/* Q8_0 block length along K ("The tensors": row b of S scales rows 32b..32b+31). */
+#define Q8_BLOCK 32
+
+/*
+ * q8_matvec -- C = A (x) dequant(W, S).
+ *   A  f32 [M, K]            activations, row-major
+ *   W  i8  [K, N]            quantized weights, one column per output
+ *   S  f32 [ceil(K/32), N]   scales; row b scales rows 32b .. min(32b+32, K)
+ *   C  f32 [M, N]            output, overwritten (K == 0 writes zeros)
+ * Errors: Q8_ERR_INVALID, Q8_ERR_TOO_LARGE, Q8_ERR_UNSUPPORTED_DEVICE,
+ * Q8_ERR_HIP.  Deterministic: the same inputs give bitwise-equal outputs.
+ */
+q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
+                    int64_t M, int64_t K, int64_t N, void *stream);
+
+/*
+ * Launch plan of q8_matvec.  Every field 0 means "choose automatically".
+ *   vec     columns (= bytes of W) each lane loads per row: 16, 8, 4, 2 or 1.
+ *           N must be a multiple of vec, W 'vec'-byte aligned and S
+ *           min(16, 4*vec)-byte aligned.
+ *   m_tile  activation rows per pass: 1, 2, 4 or 8, with m_tile*vec <= 32.
+ *   splits  workgroups sharing one column tile along K (split-K), 1..ceil(K/32).
+ *   waves   waves per workgroup; 4 is the only value supported.
+ */
+typedef struct q8_plan {
+  int32_t vec;
+  int32_t m_tile;
+  int32_t splits;
+  int32_t waves;
+} q8_plan;
+
+/*
+ * q8_matvec_choose_plan -- host-only: the plan q8_matvec would use for these
+ * extents on a device with `num_cus` compute units, given the byte
+ * alignment of W's and S's addresses (pass the pointers' low bits, or 256
+ * for allocator-aligned buffers).  Fills *out.  Touches no device.
+ * Errors: Q8_ERR_INVALID (bad extents, num_cus < 1, out == NULL).
+ */
+q8_status q8_matvec_choose_plan(int64_t M, int64_t K, int64_t N,
+                                int64_t w_align, int64_t s_align,
+                                int32_t num_cus, q8_plan *out);
+
+/*
+ * q8_matvec_with_plan -- q8_matvec with explicit launch parameters (zero
+ * fields are chosen automatically).  Results are equal for every valid plan
+ * up to the f32 rounding of the summation order; a fixed plan is
+ * deterministic.  Errors: as q8_matvec; Q8_ERR_INVALID for an unsupported
+ * plan.
+ */
+q8_status q8_matvec_with_plan(const float *A, const int8_t *W, const float *S, float *C,
+                              int64_t M, int64_t K, int64_t N, const q8_plan *plan,
+                              void *stream);
+
+/*
+ * q8_dot_t -- C = A @ W^T in exact integer arithmetic.
+ *   A  i8  [M, K]   row-major
+ *   W  i8  [N, K]   row-major, one output row per row (K contiguous)
+ *   C  i32 [M, N]   overwritten; each element is the exact sum reduced modulo
+ *                   2^32 (exact whenever |sum| < 2^31, e.g. K <= 131071)
+ * Errors: Q8_ERR_INVALID, Q8_ERR_TOO_LARGE, Q8_ERR_UNSUPPORTED_DEVICE,
+ * Q8_ERR_HIP.
+ */
+q8_status q8_dot_t(const int8_t *A, const int8_t *W, int32_t *C,
+                   int64_t M, int64_t K, int64_t N, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *q8_status_string(q8_status s);
+
+/* The hipError_t behind the calling thread's most recent Q8_ERR_HIP (0 if none). */
+int q8_last_hip_error(void);
+
+/* Frees every library-owned workspace after synchronising the device(s) that
+ * own one.  Safe to call at any time when no call is in flight. */
+void q8_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8_GEMV_H */

@@ -1,0 +1,183 @@
+"""Thin Python binding of libq8gemv.so (include/q8_gemv.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  torch supplies device memory and the stream.  If the library is not
+built this module raises; there is no fallback implementation.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+Q8_OK = 0
+Q8_ERR_INVALID = 1
+Q8_ERR_TOO_LARGE = 2
+Q8_ERR_UNSUPPORTED_DEVICE = 3
+Q8_ERR_HIP = 4
+
+BLOCK = 32
+
+#: Every symbol include/q8_gemv.h declares.
+EXPORTED = (
+    "q8_matvec",
+    "q8_matvec_with_plan",
+    "q8_matvec_choose_plan",
+    "q8_dot_t",
+    "q8_status_string",
+    "q8_last_hip_error",
+    "q8_release",
+)
+
+
+class Q8Plan(ctypes.Structure):
+    _fields_ = [("vec", ctypes.c_int32), ("m_tile", ctypes.c_int32),
+                ("splits", ctypes.c_int32), ("waves", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {"vec": self.vec, "m_tile": self.m_tile, "splits": self.splits, "waves": self.waves}
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = f"{what}: {q8_status_string(status)}"
+        if status == Q8_ERR_HIP:
+            msg += f" (hipError {q8_last_hip_error()})"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def load():
+    """The loaded library (ctypes.CDLL), loading it on first use."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m quantized_decode_gemv_q8_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.q8_matvec.argtypes = [p, p, p, p, i64, i64, i64, p]
+    L.q8_matvec.restype = ctypes.c_int
+    L.q8_matvec_with_plan.argtypes = [p, p, p, p, i64, i64, i64, ctypes.POINTER(Q8Plan), p]
+    L.q8_matvec_with_plan.restype = ctypes.c_int
+    L.q8_matvec_choose_plan.argtypes = [i64, i64, i64, i64, i64, i32, ctypes.POINTER(Q8Plan)]
+    L.q8_matvec_choose_plan.restype = ctypes.c_int
+    L.q8_dot_t.argtypes = [p, p, p, i64, i64, i64, p]
+    L.q8_dot_t.restype = ctypes.c_int
+    L.q8_status_string.argtypes = [ctypes.c_int]
+    L.q8_status_string.restype = ctypes.c_char_p
+    L.q8_last_hip_error.argtypes = []
+    L.q8_last_hip_error.restype = ctypes.c_int
+    L.q8_release.argtypes = []
+    L.q8_release.restype = None
+    _lib = L
+    return L
+
+
+def q8_status_string(status):
+    return load().q8_status_string(int(status)).decode()
+
+
+def q8_last_hip_error():
+    return load().q8_last_hip_error()
+
+
+def q8_release():
+    load().q8_release()
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensor(name, t, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense row-major)")
+
+
+def _q8_args(A, W, S, out):
+    if A.dim() != 2 or W.dim() != 2:
+        raise ValueError("A must be [M,K] and W [K,N]")
+    M, K = A.shape
+    N = W.shape[1]
+    KB = (K + BLOCK - 1) // BLOCK
+    _check_tensor("A", A, torch.float32, (M, K))
+    _check_tensor("W", W, torch.int8, (K, N))
+    _check_tensor("S", S, torch.float32, (KB, N))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _check_tensor("out", out, torch.float32, (M, N))
+    for t in (W, S, out):
+        if t.device != A.device:
+            raise ValueError("all tensors must be on one device")
+    return M, K, N, out
+
+
+def q8_matvec(A, W, S, out=None, stream=None):
+    """C[m,n] = sum_k A[m,k] W[k,n] S[k//32,n] on the GPU; returns C (f32 [M,N])."""
+    M, K, N, out = _q8_args(A, W, S, out)
+    with torch.cuda.device(A.device):
+        st = load().q8_matvec(A.data_ptr(), W.data_ptr(), S.data_ptr(), out.data_ptr(),
+                              M, K, N, _stream_handle(stream, A.device))
+    if st != Q8_OK:
+        raise Q8Error(st, "q8_matvec")
+    return out
+
+
+def q8_matvec_with_plan(A, W, S, plan, out=None, stream=None):
+    """q8_matvec with an explicit launch plan (dict with vec, m_tile, splits, waves)."""
+    M, K, N, out = _q8_args(A, W, S, out)
+    pl = Q8Plan(int(plan.get("vec", 0)), int(plan.get("m_tile", 0)),
+                int(plan.get("splits", 0)), int(plan.get("waves", 0)))
+    with torch.cuda.device(A.device):
+        st = load().q8_matvec_with_plan(A.data_ptr(), W.data_ptr(), S.data_ptr(), out.data_ptr(),
+                                        M, K, N, ctypes.byref(pl), _stream_handle(stream, A.device))
+    if st != Q8_OK:
+        raise Q8Error(st, "q8_matvec_with_plan")
+    return out
+
+
+def q8_matvec_choose_plan(M, K, N, w_align=256, s_align=256, num_cus=256):
+    """The plan q8_matvec would pick (host logic only; touches no device)."""
+    pl = Q8Plan()
+    st = load().q8_matvec_choose_plan(int(M), int(K), int(N), int(w_align), int(s_align),
+                                      int(num_cus), ctypes.byref(pl))
+    if st != Q8_OK:
+        raise Q8Error(st, "q8_matvec_choose_plan")
+    return pl.as_dict()
+
+
+def q8_dot_t(A, W, out=None, stream=None):
+    """C[m,n] = sum_k A[m,k] W[n,k] in exact i32 on the GPU; returns C (i32 [M,N])."""
+    if A.dim() != 2 or W.dim() != 2:
+        raise ValueError("A must be [M,K] and W [N,K]")
+    M, K = A.shape
+    N = W.shape[0]
+    _check_tensor("A", A, torch.int8, (M, K))
+    _check_tensor("W", W, torch.int8, (N, K))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=A.device)
+    _check_tensor("out", out, torch.int32, (M, N))
+    if W.device != A.device or out.device != A.device:
+        raise ValueError("all tensors must be on one device")
+    with torch.cuda.device(A.device):
+        st = load().q8_dot_t(A.data_ptr(), W.data_ptr(), out.data_ptr(), M, K, N,
+                             _stream_handle(stream, A.device))
+    if st != Q8_OK:
+        raise Q8Error(st, "q8_dot_t")
+    return out

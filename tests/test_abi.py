@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, plans launches on the host, and rejects bad arguments before
+touching a device."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from quantized_decode_gemv_q8_amd import binding
+from quantized_decode_gemv_q8_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8_gemv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH), reason="libq8gemv.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert header_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(5):
+        s = binding.q8_status_string(code)
+        assert s.startswith("Q8_")
+    assert binding.q8_status_string(99) == "unknown q8_status"
+    assert binding.q8_last_hip_error() == 0
+
+
+# ------------------------------------------------------------------ plan (host logic)
+
+def plan(M, K, N, w_align=256, s_align=256, cus=256):
+    return binding.q8_matvec_choose_plan(M, K, N, w_align, s_align, cus)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 128), (1, 4096, 4096), (1, 8192, 28672), (1, 28672, 8192),
+                                   (4, 4100, 5000), (3, 33, 7), (9, 1000, 17), (16, 64, 64), (1, 1, 1)])
+def test_plan_is_valid_and_normalised(M, K, N):
+    p = plan(M, K, N)
+    KB = math.ceil(K / 32)
+    assert p["vec"] in (16, 8, 4, 2, 1) and N % p["vec"] == 0
+    assert p["m_tile"] in (1, 2, 4, 8) and p["m_tile"] * p["vec"] <= 32
+    assert p["waves"] == 4
+    assert 1 <= p["splits"] <= KB
+    bps = math.ceil(KB / p["splits"])
+    assert math.ceil(KB / bps) == p["splits"]  # every split holds at least one block
+    assert p["m_tile"] * bps * 32 <= 256 * 8  # activations fit the staging registers
+
+
+def test_plan_vec_follows_shape_and_alignment():
+    assert plan(1, 4096, 4096)["vec"] == 16
+    assert plan(4, 4100, 5000)["vec"] == 8      # 5000 % 16 == 8, and 4 rows * 8 <= 32
+    assert plan(1, 64, 4096, w_align=4)["vec"] == 4
+    assert plan(1, 64, 4096, s_align=8)["vec"] == 2
+    assert plan(1, 64, 7)["vec"] == 1
+    assert plan(8, 64, 4096)["vec"] == 4       # 8 rows: 8 * vec <= 32
+    assert plan(2, 64, 4096)["m_tile"] == 2
+
+
+def test_plan_splits_fill_the_device():
+    p = plan(1, 8192, 28672)
+    tiles = math.ceil(28672 / (64 * p["vec"]))
+    assert tiles * p["splits"] >= 256           # at least one workgroup per CU
+    small = plan(1, 8192, 28672, cus=8)
+    assert small["splits"] <= p["splits"]
+
+
+def test_plan_rejects_bad_arguments():
+    L = binding.load()
+    out = binding.Q8Plan()
+    assert L.q8_matvec_choose_plan(-1, 4, 4, 256, 256, 256, ctypes.byref(out)) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec_choose_plan(1, 4, 4, 256, 256, 0, ctypes.byref(out)) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec_choose_plan(1, 4, 4, 256, 256, 256, None) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec_choose_plan(1, 1 << 16, 1 << 15, 256, 256, 256, ctypes.byref(out)) == binding.Q8_ERR_TOO_LARGE
+
+
+# ------------------------------------------------------------------ argument validation
+# Every call below is rejected (or is a no-op) before the library touches HIP.
+
+def test_matvec_rejects_bad_extents_and_pointers():
+    L = binding.load()
+    fake = ctypes.c_void_p(0x1000)
+    null = None
+    assert L.q8_matvec(fake, fake, fake, fake, -1, 4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec(fake, fake, fake, fake, 1, -4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec(null, fake, fake, fake, 1, 4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec(fake, null, fake, fake, 1, 4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec(fake, fake, null, fake, 1, 4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec(fake, fake, fake, null, 1, 4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_matvec(fake, fake, fake, fake, 1, 1 << 16, 1 << 15, null) == binding.Q8_ERR_TOO_LARGE
+    # empty outputs are a no-op: nothing is read, nothing is launched
+    assert L.q8_matvec(null, null, null, null, 0, 4, 4, null) == binding.Q8_OK
+    assert L.q8_matvec(null, null, null, null, 3, 4, 0, null) == binding.Q8_OK
+    assert L.q8_matvec_with_plan(fake, fake, fake, fake, 1, 4, 4, None, null) == binding.Q8_ERR_INVALID
+
+
+def test_dot_t_rejects_bad_extents_and_pointers():
+    L = binding.load()
+    fake = ctypes.c_void_p(0x1000)
+    null = None
+    assert L.q8_dot_t(fake, fake, fake, 1, -1, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_dot_t(null, fake, fake, 1, 4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_dot_t(fake, null, fake, 1, 4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_dot_t(fake, fake, null, 1, 4, 4, null) == binding.Q8_ERR_INVALID
+    assert L.q8_dot_t(fake, fake, fake, 1 << 16, 1 << 16, 4, null) == binding.Q8_ERR_TOO_LARGE
+    assert L.q8_dot_t(null, null, null, 0, 4, 4, null) == binding.Q8_OK
+
+
+def test_release_without_work_is_safe():
+    binding.q8_release()
