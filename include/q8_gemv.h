@@ -72,13 +72,17 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
  *           N must be a multiple of vec, W 'vec'-byte aligned and S
  *           min(16, 4*vec)-byte aligned.
  *   m_tile  activation rows per pass: 1, 2, 4 or 8, with m_tile*vec <= 32.
- *   splits  workgroups sharing one column tile along K (split-K), 1..ceil(K/32).
+ *   workgroups  workgroups per pass over W.  W is cut into column tiles of
+ *           64*vec columns and groups of four 32-row blocks along K; the
+ *           (tile, group) units are dealt to the workgroups in contiguous runs
+ *           of equal length (within one), at most 16/m_tile units each.  A
+ *           tile shared by several workgroups is combined in K order.
  *   waves   waves per workgroup; 4 is the only value supported.
  */
 typedef struct q8_plan {
   int32_t vec;
   int32_t m_tile;
-  int32_t splits;
+  int32_t workgroups;
   int32_t waves;
 } q8_plan;
 

@@ -34,10 +34,10 @@ EXPORTED = (
 
 class Q8Plan(ctypes.Structure):
     _fields_ = [("vec", ctypes.c_int32), ("m_tile", ctypes.c_int32),
-                ("splits", ctypes.c_int32), ("waves", ctypes.c_int32)]
+                ("workgroups", ctypes.c_int32), ("waves", ctypes.c_int32)]
 
     def as_dict(self):
-        return {"vec": self.vec, "m_tile": self.m_tile, "splits": self.splits, "waves": self.waves}
+        return {"vec": self.vec, "m_tile": self.m_tile, "workgroups": self.workgroups, "waves": self.waves}
 
 
 class Q8Error(RuntimeError):
@@ -140,10 +140,10 @@ def q8_matvec(A, W, S, out=None, stream=None):
 
 
 def q8_matvec_with_plan(A, W, S, plan, out=None, stream=None):
-    """q8_matvec with an explicit launch plan (dict with vec, m_tile, splits, waves)."""
+    """q8_matvec with an explicit launch plan (dict with vec, m_tile, workgroups, waves)."""
     M, K, N, out = _q8_args(A, W, S, out)
     pl = Q8Plan(int(plan.get("vec", 0)), int(plan.get("m_tile", 0)),
-                int(plan.get("splits", 0)), int(plan.get("waves", 0)))
+                int(plan.get("workgroups", 0)), int(plan.get("waves", 0)))
     with torch.cuda.device(A.device):
         st = load().q8_matvec_with_plan(A.data_ptr(), W.data_ptr(), S.data_ptr(), out.data_ptr(),
                                         M, K, N, ctypes.byref(pl), _stream_handle(stream, A.device))

@@ -23,8 +23,11 @@ q8_status hip_status(hipError_t e) {
 
 constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // 32-bit signed element offsets
 
-// Workgroups per CU the automatic split targets (4-wave workgroups).
-constexpr int kTargetWgsPerCu = 3;
+// Automatic plans give every CU one 4-wave workgroup with an equal share of W:
+// each wave keeps three chunks of rows in flight, which is enough to stream
+// at full rate, and a second workgroup per CU finishes later than the first
+// (the older one wins issue arbitration), leaving a tail.
+constexpr int kTargetWgsPerCu = 1;
 
 struct DevInfo {
   bool gfx950;
@@ -82,32 +85,66 @@ bool vec_fits(int vec, int64_t N, int64_t w_align, int64_t s_align) {
   return N % vec == 0 && w_align % vec == 0 && s_align % s_need == 0;
 }
 
-// Fills in the split count of a plan whose vec and m_tile are set, and
-// normalises it so that every split is non-empty.  Returns false if the plan
-// cannot run.
-bool finish_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan *pl) {
-  const int64_t KB = ceil_div(K, kBlock);
-  const int64_t n_tiles = ceil_div(N, 64 * (int64_t)pl->vec);
-  const int64_t m_chunks = ceil_div(M, pl->m_tile);
-  const int64_t bps_max = (int64_t)q8::kThreads * 8 / ((int64_t)pl->m_tile * kBlock);
-  int64_t splits = pl->splits;
-  if (splits == 0) {
-    const int64_t target = (int64_t)num_cus * kTargetWgsPerCu;
-    splits = target / (n_tiles * m_chunks);
-    if (splits < 1) splits = 1;
-    if (splits > KB) splits = KB;
-    int64_t bps = ceil_div(KB, splits);
-    if (bps > q8::kWaves) bps = ceil_div(bps, q8::kWaves) * q8::kWaves;  // whole rounds of the 4 waves
-    if (bps > bps_max) bps = bps_max;
-    splits = ceil_div(KB, bps);
+// Launch layout derived from a plan: the (tile, group) units of W are dealt
+// in contiguous runs to n_wg workgroups per pass over W.
+struct Layout {
+  int64_t KB, G, n_tiles, m_chunks, units, n_wg, upw, rem, count_max, cmax;
+};
+
+int64_t wg_of_unit(int64_t u, int64_t upw, int64_t rem) {
+  const int64_t big = rem * (upw + 1);
+  return u < big ? u / (upw + 1) : rem + (u - big) / upw;
+}
+
+Layout make_layout(int64_t M, int64_t K, int64_t N, const q8_plan &pl, int64_t n_wg) {
+  Layout L;
+  L.KB = ceil_div(K, kBlock);
+  L.G = ceil_div(L.KB, q8::kWaves);
+  L.n_tiles = ceil_div(N, 64 * (int64_t)pl.vec);
+  L.m_chunks = ceil_div(M, pl.m_tile);
+  L.units = L.n_tiles * L.G;
+  L.n_wg = n_wg;
+  L.upw = n_wg > 0 ? L.units / n_wg : 0;
+  L.rem = n_wg > 0 ? L.units % n_wg : 0;
+  L.count_max = L.upw + (L.rem > 0 ? 1 : 0);
+  L.cmax = 0;
+  if (n_wg > 0 && L.upw > 0) {
+    for (int64_t t = 0; t < L.n_tiles; ++t) {
+      const int64_t c = wg_of_unit(t * L.G + L.G - 1, L.upw, L.rem) - wg_of_unit(t * L.G, L.upw, L.rem) + 1;
+      if (c > L.cmax) L.cmax = c;
+    }
   }
-  if (splits < 1 || splits > KB) return false;
-  int64_t bps = ceil_div(KB, splits);
-  if (bps > bps_max) return false;
-  splits = ceil_div(KB, bps);
-  if (splits > 1 && splits * M * N >= kIndexLimit) return false;
-  if (q8::gemv_lds_bytes(pl->vec, pl->m_tile, (int)bps) > q8::kMaxGemvLds) return false;
-  pl->splits = (int32_t)splits;
+  return L;
+}
+
+// Fills in the workgroup count of a plan whose vec and m_tile are set.
+// Returns false if the plan cannot run.
+bool finish_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan *pl) {
+  const int64_t cap = q8::max_units_per_wg(pl->m_tile);
+  Layout L = make_layout(M, K, N, *pl, 1);
+  int64_t n_wg = pl->workgroups;
+  if (n_wg == 0) {
+    int64_t target = (int64_t)num_cus * kTargetWgsPerCu / L.m_chunks;
+    if (target < 1) target = 1;
+    n_wg = L.units < target ? L.units : target;
+    if (ceil_div(L.units, n_wg) > cap) n_wg = ceil_div(L.units, cap);
+    // Short tiles (few groups) make runs span many tiles: keep their parked
+    // sums within the LDS budget.
+    while (n_wg < L.units) {
+      const int count = (int)ceil_div(L.units, n_wg);
+      const int nseg = q8::max_segments(count, (int)L.G);
+      if (nseg <= 32 && q8::gemv_lds_bytes(pl->vec, pl->m_tile, count, nseg) <= q8::kMaxGemvLds) break;
+      ++n_wg;
+    }
+  }
+  if (n_wg < 1 || n_wg > L.units) return false;
+  L = make_layout(M, K, N, *pl, n_wg);
+  if (L.count_max > cap) return false;
+  if (L.m_chunks * L.n_tiles * L.cmax * pl->m_tile * 64 * pl->vec >= kIndexLimit) return false;
+  const int nseg = q8::max_segments((int)L.count_max, (int)L.G);
+  if (nseg > 32) return false;  // one bit per segment in the kernel's arrival mask
+  if (q8::gemv_lds_bytes(pl->vec, pl->m_tile, (int)L.count_max, nseg) > q8::kMaxGemvLds) return false;
+  pl->workgroups = (int32_t)n_wg;
   pl->waves = q8::kWaves;
   return true;
 }
@@ -123,7 +160,9 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t w_align, int64_t
   if (pl.m_tile == 0) pl.m_tile = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
   if (pl.m_tile != 1 && pl.m_tile != 2 && pl.m_tile != 4 && pl.m_tile != 8) return Q8_ERR_INVALID;
   if (pl.vec == 0) {
-    for (int v = 16; v >= 1; v >>= 1) {
+    // 8-byte lanes (512-column tiles) measure best on MI355X for the decode
+    // shapes; 16 is used only when asked for.
+    for (int v = 8; v >= 1; v >>= 1) {
       if (v * pl.m_tile <= 32 && vec_fits(v, N, w_align, s_align)) {
         pl.vec = v;
         break;
@@ -133,7 +172,7 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t w_align, int64_t
   }
   if (pl.vec != 16 && pl.vec != 8 && pl.vec != 4 && pl.vec != 2 && pl.vec != 1) return Q8_ERR_INVALID;
   if (pl.vec * pl.m_tile > 32 || !vec_fits(pl.vec, N, w_align, s_align)) return Q8_ERR_INVALID;
-  if (pl.splits < 0) return Q8_ERR_INVALID;
+  if (pl.workgroups < 0) return Q8_ERR_INVALID;
   if (K > 0 && !finish_plan(M, K, N, num_cus, &pl)) return Q8_ERR_INVALID;
   *out = pl;
   return Q8_OK;
@@ -196,31 +235,34 @@ q8_status matvec_impl(const float *A, const int8_t *W, const float *S, float *C,
   st = resolve_plan(M, K, N, address_alignment(W), address_alignment(S), info.cus, req, &pl);
   if (st != Q8_OK) return st;
 
+  const Layout L = make_layout(M, K, N, pl, pl.workgroups);
   q8::GemvArgs a;
   a.A = A;
   a.W = W;
   a.S = S;
   a.C = C;
-  a.partial = nullptr;
-  a.counters = nullptr;
   a.M = (int)M;
   a.K = (int)K;
   a.N = (int)N;
-  a.KB = (int)KB;
-  a.n_tiles = (int)ceil_div(N, 64 * (int64_t)pl.vec);
-  a.splits = pl.splits;
-  a.bps = (int)ceil_div(KB, pl.splits);
-  a.pitch = q8::padded_pitch(a.bps * kBlock, 4);
-  const int m_chunks = (int)ceil_div(M, pl.m_tile);
-  if (a.splits > 1) {
+  a.KB = (int)L.KB;
+  a.n_tiles = (int)L.n_tiles;
+  a.groups = (int)L.G;
+  a.n_wg = (int)L.n_wg;
+  a.upw = (int)L.upw;
+  a.rem = (int)L.rem;
+  a.cmax = (int)L.cmax;
+  a.pitch = q8::padded_pitch((int)L.count_max * kBlock, 4);
+  {
     Workspace ws;
-    st = get_workspace(dev, stream, (size_t)a.splits * M * N, (size_t)m_chunks * a.n_tiles, &ws);
+    st = get_workspace(dev, stream, (size_t)(L.m_chunks * L.n_tiles * L.cmax * pl.m_tile * 64 * pl.vec),
+                       (size_t)(L.m_chunks * L.n_tiles), &ws);
     if (st != Q8_OK) return st;
     a.partial = ws.partial;
     a.counters = ws.counters;
   }
-  const size_t lds = q8::gemv_lds_bytes(pl.vec, pl.m_tile, a.bps);
-  return hip_status(q8::launch_gemv(pl.vec, pl.m_tile, a, m_chunks, lds, stream));
+  const size_t lds = q8::gemv_lds_bytes(pl.vec, pl.m_tile, (int)L.count_max,
+                                       q8::max_segments((int)L.count_max, (int)L.G));
+  return hip_status(q8::launch_gemv(pl.vec, pl.m_tile, a, (int)L.m_chunks, lds, stream));
 }
 
 }  // namespace

@@ -23,19 +23,23 @@ __host__ __device__ constexpr int padded_pitch(int cols, int elem_bytes) {
   return (cols * elem_bytes) % kLdsBankPeriodBytes == 0 ? cols + 8 : cols;
 }
 
-// Arguments of the Q8_0 matvec kernel (one launch).
+// Arguments of the Q8_0 matvec kernel (one launch).  The (column tile,
+// 4-block group) units of W, tile-major, are dealt to the n_wg workgroups of a
+// pass in contiguous runs: upw units each, one more for the first rem.
 struct GemvArgs {
   const float *A;        // [M, K]
   const int8_t *W;       // [K, N]
   const float *S;        // [KB, N]
   float *C;              // [M, N]
-  float *partial;        // [splits, M, N] split-K partial sums (splits > 1)
+  float *partial;        // [m_chunks][n_tiles][cmax][m_tile * 64 * vec] partial sums
   uint32_t *counters;    // [m_chunks * n_tiles] arrival counters, zero between calls
   int M, K, N, KB;
   int n_tiles;           // column tiles of 64 * vec columns
-  int splits;            // workgroups per column tile along K
-  int bps;               // blocks per split
-  int pitch;             // LDS row pitch of the staged activations, in floats
+  int groups;            // groups of four K blocks per tile: ceil(KB / 4)
+  int n_wg;              // workgroups per pass (per chunk of m_tile rows of A)
+  int upw, rem;          // units per workgroup
+  int cmax;              // most workgroups that share one tile
+  int pitch;             // row pitch of a wave's activation stage in LDS, floats
 };
 
 // Launches the Q8_0 matvec kernel instance (vec, m_tile) on `stream`.
@@ -46,15 +50,26 @@ hipError_t launch_gemv(int vec, int m_tile, const GemvArgs &args, int m_chunks,
 // Writes `n` zero words at `p` (used for K == 0 outputs and fresh counters).
 hipError_t launch_zero_fill(void *p, size_t n_words, hipStream_t stream);
 
-// Largest LDS footprint (bytes) the matvec kernel may be given.
-constexpr size_t kMaxGemvLds = 64 * 1024;
+// Largest dynamic LDS footprint (bytes) the matvec kernel may be given: a
+// gfx950 workgroup may use the CU's 160 KB; 1 KB stays for static LDS.
+constexpr size_t kMaxGemvLds = 159 * 1024;
 
-// LDS bytes the matvec kernel needs for a plan.
-inline size_t gemv_lds_bytes(int vec, int m_tile, int bps) {
-  size_t stage = (size_t)m_tile * padded_pitch(bps * kBlock, 4) * 4;
-  size_t red = (size_t)kWaves * m_tile * 64 * vec * 4;
-  return stage > red ? stage : red;
+// Most (tile, group) units one workgroup may take at a given m_tile: a wave
+// stages m_tile * units * 32 activations from 8 registers per lane.
+constexpr int max_units_per_wg(int m_tile) { return 64 * 8 / (m_tile * kBlock); }
+
+// LDS bytes the matvec kernel needs: four private activation stages of
+// m_tile rows of `count` blocks, and parked sums for `nseg` tiles (the most
+// tiles one workgroup's run touches) from each of the four waves.
+inline size_t gemv_lds_bytes(int vec, int m_tile, int count, int nseg) {
+  const size_t stage = (size_t)kWaves * m_tile * padded_pitch(count * kBlock, 4) * 4;
+  const size_t slots = (size_t)nseg * kWaves * m_tile * 64 * vec * 4;
+  return stage + slots;
 }
+
+// Most tiles a run of `count` (tile, group) units touches, with `groups`
+// groups per tile.
+constexpr int max_segments(int count, int groups) { return (count - 1 + groups - 1) / groups + 1; }
 
 // Arguments of the i8 dot_t kernels.
 struct DotArgs {

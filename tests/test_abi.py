@@ -56,15 +56,16 @@ def test_plan_is_valid_and_normalised(M, K, N):
     assert p["vec"] in (16, 8, 4, 2, 1) and N % p["vec"] == 0
     assert p["m_tile"] in (1, 2, 4, 8) and p["m_tile"] * p["vec"] <= 32
     assert p["waves"] == 4
-    assert 1 <= p["splits"] <= KB
-    bps = math.ceil(KB / p["splits"])
-    assert math.ceil(KB / bps) == p["splits"]  # every split holds at least one block
-    assert p["m_tile"] * bps * 32 <= 256 * 8  # activations fit the staging registers
+    units = math.ceil(N / (64 * p["vec"])) * math.ceil(KB / 4)  # (column tile, 4-block group) units
+    assert 1 <= p["workgroups"] <= units        # every workgroup holds at least one unit
+    count_max = math.ceil(units / p["workgroups"])
+    assert p["m_tile"] * count_max * 32 <= 64 * 8  # a wave's activations fit its staging registers
 
 
 def test_plan_vec_follows_shape_and_alignment():
-    assert plan(1, 4096, 4096)["vec"] == 16
-    assert plan(4, 4100, 5000)["vec"] == 8      # 5000 % 16 == 8, and 4 rows * 8 <= 32
+    assert plan(1, 4096, 4096)["vec"] == 8      # automatic plans use at most 8-byte lanes
+    assert plan(4, 4100, 5000)["vec"] == 8      # 5000 % 8 == 0, and 4 rows * 8 <= 32
+    assert plan(1, 64, 4100)["vec"] == 4
     assert plan(1, 64, 4096, w_align=4)["vec"] == 4
     assert plan(1, 64, 4096, s_align=8)["vec"] == 2
     assert plan(1, 64, 7)["vec"] == 1
@@ -72,12 +73,15 @@ def test_plan_vec_follows_shape_and_alignment():
     assert plan(2, 64, 4096)["m_tile"] == 2
 
 
-def test_plan_splits_fill_the_device():
-    p = plan(1, 8192, 28672)
-    tiles = math.ceil(28672 / (64 * p["vec"]))
-    assert tiles * p["splits"] >= 256           # at least one workgroup per CU
+def test_plan_workgroups_fill_the_device():
+    for M, K, N in [(1, 8192, 28672), (1, 28672, 8192)]:
+        p = plan(M, K, N)
+        assert p["workgroups"] == 256               # one workgroup per CU
+        units = math.ceil(N / (64 * p["vec"])) * math.ceil(math.ceil(K / 32) / 4)
+        assert units % p["workgroups"] == 0         # equal work for every workgroup at these shapes
+    assert plan(1, 4096, 4096)["workgroups"] == 256  # all 256 units, one each
     small = plan(1, 8192, 28672, cus=8)
-    assert small["splits"] <= p["splits"]
+    assert small["workgroups"] == 16 * 2 or math.ceil(3584 / small["workgroups"]) <= 16
 
 
 def test_plan_rejects_bad_arguments():

@@ -89,24 +89,36 @@ def test_rows(M):
 PLANS = [(v, mt) for v in (16, 8, 4, 2, 1) for mt in (1, 2, 4, 8) if v * mt <= 32]
 
 
+def units_of(M, K, N, vec):
+    return math.ceil(N / (64 * vec)) * math.ceil(math.ceil(K / 32) / 4)
+
+
 @pytest.mark.parametrize("vec,m_tile", PLANS)
 def test_every_instance(vec, m_tile):
-    M, K, N = 5, 1000, 2048  # KB = 32 with an 8-row remainder; two m passes at m_tile < 5
+    M, K, N = 5, 3000, 2048  # KB = 94 (24-row remainder), 24 groups; two m passes at m_tile < 5
     A, W, S = rand_q8(M, K, N, (103, vec, m_tile))
-    KB = math.ceil(K / 32)
-    bps_max = 64 // m_tile
-    for splits in sorted({1, 2, 3, 7, KB, math.ceil(KB / bps_max)}):
-        if math.ceil(KB / splits) > bps_max:
+    units = units_of(M, K, N, vec)
+    cap = 16 // m_tile
+    ran = 0
+    for n_wg in sorted({1, 2, 3, 5, 7, 23, 24, 25, units // 2, units - 1, units, math.ceil(units / cap)}):
+        if not 1 <= n_wg <= units or math.ceil(units / n_wg) > cap:
             continue
-        C = gpu_q8(A, W, S, plan={"vec": vec, "m_tile": m_tile, "splits": splits})
+        try:
+            C = gpu_q8(A, W, S, plan={"vec": vec, "m_tile": m_tile, "workgroups": n_wg})
+        except binding.Q8Error as e:
+            # long runs over many tiles can exceed the LDS budget: rejected up front
+            assert e.status == binding.Q8_ERR_INVALID
+            continue
         assert_parity(A, W, S, C)
+        ran += 1
+    assert ran >= 3
 
 
 def test_invalid_plans_are_rejected():
     A, W, S = (to_dev(x) for x in rand_q8(1, 64, 100, 104))
-    # N=100 allows vec 4 at most; K=64 has 2 blocks
-    for bad in ({"vec": 16}, {"vec": 3}, {"m_tile": 3}, {"vec": 4, "m_tile": 16}, {"splits": 3},
-                {"waves": 8}, {"splits": -1}):
+    # N=100 allows vec 4 at most; K=64 has 2 blocks (one group), 2 column tiles at vec 4
+    for bad in ({"vec": 16}, {"vec": 3}, {"m_tile": 3}, {"vec": 4, "m_tile": 16}, {"workgroups": 3},
+                {"waves": 8}, {"workgroups": -1}):
         with pytest.raises(binding.Q8Error):
             binding.q8_matvec_with_plan(A, W, S, bad)
 
@@ -210,7 +222,7 @@ def test_power_of_two_scaling_is_exact():
 
 def test_rows_are_independent():
     A, W, S = rand_q8(4, 4100, 5000, 111)
-    plan = {"vec": 8, "splits": 17}  # 8 blocks per split: fits m_tile 4 and 1
+    plan = {"vec": 8, "workgroups": 165}  # 330 units, 2 per workgroup: fits m_tile 4 and 1
     C = gpu_q8(A, W, S, plan=dict(plan, m_tile=4))
     for m in range(4):
         Cm = gpu_q8(A[m:m + 1], W, S, plan=dict(plan, m_tile=1))
@@ -243,8 +255,8 @@ def test_non_default_stream():
 def test_workspace_grows_and_release():
     small = rand_q8(1, 640, 256, 114)
     big = rand_q8(4, 8192, 8192, 115)
-    assert_parity(*small, gpu_q8(*small, plan={"splits": 4}))
-    assert_parity(*big, gpu_q8(*big, plan={"splits": 16}))
-    assert_parity(*small, gpu_q8(*small, plan={"splits": 20}))
+    assert_parity(*small, gpu_q8(*small, plan={"workgroups": 4}))
+    assert_parity(*big, gpu_q8(*big, plan={"workgroups": 512}))
+    assert_parity(*small, gpu_q8(*small, plan={"workgroups": 5}))
     binding.q8_release()
     assert_parity(*big, gpu_q8(*big))
