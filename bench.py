@@ -9,8 +9,15 @@ step reads its weights from HBM rather than the 256 MB Infinity Cache.
 
 Prints ONE JSON line.  `value` is the effective HBM bandwidth on algorithmic
 bytes (K*N + 4*ceil(K/32)*N + 4*M*K + 4*M*N per step) over the whole timed
-region; `roofline.achieved` uses the average kernel duration from HIP events
-recorded around each launch on the launch stream.
+region (host clock).  `roofline.achieved` divides the same bytes by the average
+launch duration, taken from two HIP events recorded on the launch stream around
+the timed region (one launch per step, issued back to back).  A second pass
+records events around every single launch; its percentiles (`per_launch_us`)
+show the spread but include the event packets' own overhead.
+
+The default warm-up is long (400 launches, about 18 ms) because the device
+needs roughly 10 ms of sustained load before the kernel settles at its
+steady-state duration.
 """
 
 import argparse
@@ -93,46 +100,98 @@ def time_kernels(launch, steps, n_copies, torch):
 
 
 def cpu_baseline(wl, A, W, S, budget_s=12.0):
-    """The oracle as it stands, timed on the host on a column slice of the workload."""
+    """The oracle as it stands, timed on the host: whole-workload calls on copy 0,
+    repeated until about `budget_s` seconds of CPU work have been measured."""
     import oracle
     from threadpoolctl import threadpool_info
 
-    n_cols = min(wl.N, 4096)
-    Ws = np.ascontiguousarray(W[:, :n_cols])
-    Ss = np.ascontiguousarray(S[:, :n_cols])
-    from quantized_decode_gemv_q8_amd.workloads import Workload
-    sample = Workload("sample", "q8", wl.M, wl.K, n_cols, wl.a_dist, wl.w_dist, wl.seed)
-    oracle.q8_matvec(A, Ws, Ss)  # warm-up
+    oracle.q8_matvec(A, W, S)  # warm-up (page-in of the f64 temporaries)
     times = []
     t_start = time.perf_counter()
-    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 50):
+    while len(times) < 3 or time.perf_counter() - t_start < budget_s:
         t0 = time.perf_counter()
-        oracle.q8_matvec(A, Ws, Ss)
+        oracle.q8_matvec(A, W, S)
         times.append(time.perf_counter() - t0)
-    med = float(np.median(times))
+    total = sum(times)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {
-        "value": round(sample.algorithmic_bytes() / med / 1e9, 4),
+        "value": round(wl.algorithmic_bytes() * len(times) / total / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"f64 factored oracle on columns 0..{n_cols - 1} of the same M={wl.M} K={wl.K} inputs "
-                  f"(copy 0), median of {len(times)} runs ({sum(times):.1f} s of CPU work); "
-                  f"BLAS threads {threads}, numpy upcasts single-threaded",
+        "sample": f"f64 factored oracle on the whole M={wl.M} K={wl.K} N={wl.N} workload (copy 0), "
+                  f"{len(times)} calls in {total:.1f} s; BLAS threads {threads}, numpy upcasts single-threaded",
     }
+
+
+CALIB_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+
+
+def ingest_pmc(fetch_csv, write_csv, workload, kernel_path):
+    """Scales FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the workload's kernel by
+    what the same counters read for a device copy of CALIB_BYTES, and records the
+    HBM bytes per launch in profiles/traffic_counters.json."""
+    import csv
+
+    def per_kernel(path, counter):
+        sums, counts = {}, {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Kernel_Name"], row["Dispatch_Id"])
+                sums[key] = sums.get(key, 0.0) + float(row["Counter_Value"])
+        by_name = {}
+        for (name, _), v in sums.items():
+            by_name.setdefault(name, []).append(v)
+        return {k: float(np.mean(v)) for k, v in by_name.items()}
+
+    def pick(d, sub):
+        hits = [v for k, v in d.items() if sub in k]
+        if not hits:
+            raise SystemExit(f"no kernel matching {sub!r} in {sorted(d)}")
+        return hits[0]
+
+    kname = "q8_gemv_kernel" if "q8_gemv" in kernel_path else "dot_t_"
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    f_k, w_k = pick(fetch, kname), pick(write, kname)
+    f_c, w_c = pick(fetch, "copyBuffer"), pick(write, "copyBuffer")
+    ff, fw = CALIB_BYTES / (f_c * 1024.0), CALIB_BYTES / (w_c * 1024.0)
+    rec = {"kernel_sha": source_hash(kernel_path), "fetch_kib": f_k, "write_kib": w_k,
+           "copy_fetch_kib": f_c, "copy_write_kib": w_c, "copy_bytes": CALIB_BYTES,
+           "fetch_factor": ff, "write_factor": fw,
+           "bytes_per_launch": round(f_k * 1024.0 * ff + w_k * 1024.0 * fw)}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: rec}))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="mlp_up_8192x28672")
     ap.add_argument("--copies", type=int, default=0, help="rotated W/S copies (0: workload default)")
-    ap.add_argument("--plan", default="", help="vec,m_tile,splits override, e.g. 16,1,12")
+    ap.add_argument("--plan", default="", help="vec,m_tile,workgroups override, e.g. 8,1,224")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="short run for rocprofv3 --pmc: a few launches, then a device copy of known size")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="record HBM traffic per launch from two rocprofv3 --pmc counter CSVs")
     args = ap.parse_args()
+
+    if args.ingest_pmc:
+        wl_src = DOT_SRC if args.workload.startswith("dot_t") else KERNEL_SRC
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload, wl_src)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -152,8 +211,8 @@ def main():
 
     plan = None
     if args.plan:
-        v, mt, sp = (int(x) for x in args.plan.split(","))
-        plan = {"vec": v, "m_tile": mt, "splits": sp}
+        v, mt, nwg = (int(x) for x in args.plan.split(","))
+        plan = {"vec": v, "m_tile": mt, "workgroups": nwg}
 
     # Inputs: copy j drawn with its own seed, uploaded once.
     host0 = workloads.make(wl.name, 0)
@@ -205,16 +264,28 @@ def main():
                 raise SystemExit("parity check failed: dot_t differs from the oracle")
         print(f"[bench] parity ok on {len(cols)} sampled columns", file=sys.stderr, flush=True)
 
+    if args.pmc_pass:
+        for i in range(args.warmup + args.steps):
+            launch(i % n_copies)
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": wl.name, "launches": args.warmup + args.steps, "copies": 5,
+                          "copy_bytes": CALIB_BYTES}), flush=True)
+        return
+
     wall, gpu_s = time_steps(launch, args.steps, args.warmup, n_copies, torch)
     per = time_kernels(launch, args.steps, n_copies, torch)
     nbytes = wl.algorithmic_bytes()
     ms_per_step = wall * 1e3 / args.steps
     value = nbytes * args.steps / wall / 1e9
-    kern_ms = float(np.mean(per))
-    achieved = nbytes / (kern_ms * 1e-3) / 1e9
-    print(f"[bench] kernel avg {kern_ms * 1e3:.2f} us (median {np.median(per) * 1e3:.2f}, "
-          f"p10 {np.percentile(per, 10) * 1e3:.2f}, p90 {np.percentile(per, 90) * 1e3:.2f}); "
-          f"wall {ms_per_step * 1e3:.2f} us/step, events {gpu_s * 1e6 / args.steps:.2f} us/step",
+    launch_s = gpu_s / args.steps
+    achieved = nbytes / launch_s / 1e9
+    print(f"[bench] launch avg {launch_s * 1e6:.2f} us (events over the timed region); "
+          f"wall {ms_per_step * 1e3:.2f} us/step; per-launch events median {np.median(per) * 1e3:.2f}, "
+          f"p10 {np.percentile(per, 10) * 1e3:.2f}, p90 {np.percentile(per, 90) * 1e3:.2f}",
           file=sys.stderr, flush=True)
 
     traffic = measured_traffic(wl.name, kernel_src)
@@ -237,8 +308,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "step_us_events": round(gpu_s * 1e6 / args.steps, 3),
-        "kernel_us": {"mean": round(kern_ms * 1e3, 3), "median": round(float(np.median(per)) * 1e3, 3),
+        "launch_us": round(launch_s * 1e6, 3),
+        "per_launch_us": {"mean": round(float(np.mean(per)) * 1e3, 3), "median": round(float(np.median(per)) * 1e3, 3),
                       "p10": round(float(np.percentile(per, 10)) * 1e3, 3),
                       "p90": round(float(np.percentile(per, 90)) * 1e3, 3)},
     }
