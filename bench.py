@@ -34,8 +34,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E peak
-KERNEL_SRC = os.path.join(ROOT, "quantized_decode_gemv_q8_amd", "csrc", "q8_gemv.hip")
-DOT_SRC = os.path.join(ROOT, "quantized_decode_gemv_q8_amd", "csrc", "dot_t.hip")
+CSRC = os.path.join(ROOT, "quantized_decode_gemv_q8_amd", "csrc")
+# Sources whose hash stamps a traffic measurement (the kernel code itself).
+KERNEL_SRC = (os.path.join(CSRC, "q8_gemv_kernel.h"), os.path.join(CSRC, "q8_common.h"))
+DOT_SRC = (os.path.join(CSRC, "dot_t.hip"), os.path.join(CSRC, "q8_common.h"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 # Rotated copies per workload: enough to exceed the Infinity Cache (>= 1 GiB).
@@ -43,9 +45,12 @@ COPIES = {"tiny": 1, "attn4096": 57, "mlp_up_8192x28672": 4, "mlp_down_28672x819
           "ragged_m4": 47, "dot_t_16x4096x4096": 63}
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, kernel_path):
@@ -152,7 +157,7 @@ def ingest_pmc(fetch_csv, write_csv, workload, kernel_path):
             raise SystemExit(f"no kernel matching {sub!r} in {sorted(d)}")
         return hits[0]
 
-    kname = "q8_gemv_kernel" if "q8_gemv" in kernel_path else "dot_t_"
+    kname = "q8_gemv_kernel" if kernel_path is KERNEL_SRC else "dot_t_"
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     f_k, w_k = pick(fetch, kname), pick(write, kname)
     f_c, w_c = pick(fetch, "copyBuffer"), pick(write, "copyBuffer")

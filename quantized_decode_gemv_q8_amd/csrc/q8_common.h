@@ -59,12 +59,14 @@ constexpr size_t kMaxGemvLds = 159 * 1024;
 constexpr int max_units_per_wg(int m_tile) { return 64 * 8 / (m_tile * kBlock); }
 
 // LDS bytes the matvec kernel needs: four private activation stages of
-// m_tile rows of `count` blocks, and parked sums for `nseg` tiles (the most
-// tiles one workgroup's run touches) from each of the four waves.
+// m_tile rows of `count` blocks, at vec >= 8 four scale hand-over areas of
+// 64 * vec floats, and parked sums for `nseg` tiles (the most tiles one
+// workgroup's run touches) from each of the four waves.
 inline size_t gemv_lds_bytes(int vec, int m_tile, int count, int nseg) {
   const size_t stage = (size_t)kWaves * m_tile * padded_pitch(count * kBlock, 4) * 4;
+  const size_t scales = vec >= 8 ? (size_t)kWaves * 64 * vec * 4 : 0;
   const size_t slots = (size_t)nseg * kWaves * m_tile * 64 * vec * 4;
-  return stage + slots;
+  return stage + scales + slots;
 }
 
 // Most tiles a run of `count` (tile, group) units touches, with `groups`
