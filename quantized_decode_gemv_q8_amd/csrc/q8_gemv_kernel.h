@@ -51,6 +51,12 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
+// Column pieces per lane at VEC 16: two pieces of eight columns, 512 columns
+// apart, so that each W load instruction of a wave reads 512 contiguous bytes
+// of a row (eight per lane), as at VEC 8, and one workgroup reads both halves
+// of each kilobyte of the row.
+constexpr int kPiecesAt16 = 2;
+
 // Geometry of one kernel instance.
 template <int VEC>
 struct Geo {
@@ -58,6 +64,13 @@ struct Geo {
   static constexpr int kChunkRows = VEC >= 8 ? 128 / VEC : 32;    // rows per pipelined chunk
   static constexpr int kChunksPerBlock = kBlock / kChunkRows;
   static constexpr int kTileCols = 64 * VEC;
+  // A lane owns kPieces runs of kPieceCols adjacent columns; piece p of lane l
+  // starts at column 64 * kPieceCols * p + kPieceCols * l of the tile.
+  static constexpr int kPieces = VEC == 16 ? kPiecesAt16 : 1;
+  static constexpr int kPieceCols = VEC / kPieces;
+  __device__ static constexpr int col(int lane, int v) {
+    return 64 * kPieceCols * (v / kPieceCols) + kPieceCols * lane + v % kPieceCols;
+  }
   // At VEC >= 8 a lane's scales (4*VEC contiguous bytes) would take VEC/4
   // 16-byte loads strided across the wave.  Instead the wave loads the S row
   // of its tile with fully coalesced 16-byte loads (lane l takes columns
@@ -90,20 +103,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 }
 
 template <int VEC>
-__device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
-                                       uint32_t (&w)[Geo<VEC>::kWords]) {
-  if constexpr (VEC == 16) {
-    const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kStreamPolicy);
-    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-  } else if constexpr (VEC == 8) {
-    const v2u x = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kStreamPolicy);
-    w[0] = x.x; w[1] = x.y;
-  } else if constexpr (VEC == 4) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kStreamPolicy);
-  } else if constexpr (VEC == 2) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, kStreamPolicy);
-  } else {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b8(rs, voff, soff, kStreamPolicy);
+__device__ __forceinline__ void load_w(__amdgpu_buffer_rsrc_t rs, const uint32_t (&voff)[Geo<VEC>::kPieces],
+                                       uint32_t soff, uint32_t (&w)[Geo<VEC>::kWords]) {
+  constexpr int PC = Geo<VEC>::kPieceCols;
+#pragma unroll
+  for (int p = 0; p < Geo<VEC>::kPieces; ++p) {
+    if constexpr (PC == 16) {
+      const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[p], soff, kStreamPolicy);
+      w[4 * p] = x.x; w[4 * p + 1] = x.y; w[4 * p + 2] = x.z; w[4 * p + 3] = x.w;
+    } else if constexpr (PC == 8) {
+      const v2u x = __builtin_amdgcn_raw_buffer_load_b64(rs, voff[p], soff, kStreamPolicy);
+      w[2 * p] = x.x; w[2 * p + 1] = x.y;
+    } else if constexpr (PC == 4) {
+      w[p] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff[p], soff, kStreamPolicy);
+    } else if constexpr (PC == 2) {
+      w[p] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff[p], soff, kStreamPolicy);
+    } else {
+      w[p] = __builtin_amdgcn_raw_buffer_load_b8(rs, voff[p], soff, kStreamPolicy);
+    }
   }
 }
 
@@ -190,7 +207,7 @@ struct WaveStream {
   static_assert(DEPTH >= 2, "at least one chunk in flight");
 
   __amdgpu_buffer_rsrc_t w_rs, s_rs;
-  int K, N, KB, groups, wave, lane_col, pitch, last_chunk;
+  int K, N, KB, groups, wave, pitch, last_chunk;
   const float *a_lds;  // the wave's activation stage: [MT][pitch], block j at 32 j
   float *s_lds;        // the wave's scale hand-over area: 64 * VEC floats (VEC >= 8)
   int lane;
@@ -198,7 +215,7 @@ struct WaveStream {
   float *slots;        // parked sums: slot q at slots + q * 4 * MT * TW (+ wave * MT * TW)
   int it, ig;          // tile and group of the next block to issue
   int cg, cslot;       // group of the block being used, next free slot
-  uint32_t col_off;    // lane byte offset into a W row for the block being issued
+  uint32_t col_off[G::kPieces];  // lane byte offsets (per piece) into a W row for the block being issued
   int b_issue;         // that block
   uint32_t w[kDepth][CR][NWD];
   float s[kDepth][VEC];
@@ -212,8 +229,11 @@ struct WaveStream {
     if constexpr (H == 0) {
       // Columns past N (ragged last tile) load column 0 instead; blocks past
       // KB (in the last group of K) load row K-1 with zero activations.
-      const int col = it * TW + lane_col;
-      col_off = col < N ? (uint32_t)col : 0u;
+#pragma unroll
+      for (int q = 0; q < G::kPieces; ++q) {
+        const int col = it * TW + G::col(lane, q * G::kPieceCols);
+        col_off[q] = col < N ? (uint32_t)col : 0u;
+      }
       if constexpr (G::kSwizzleScales) {
 #pragma unroll
         for (int i = 0; i < G::kScaleLoads; ++i) {
@@ -242,7 +262,7 @@ struct WaveStream {
           s[BUF][4 * i + 3] = __uint_as_float(x.w);
         }
       } else {
-        load_s<VEC>(s_rs, col_off * 4u, s_row, s[BUF]);
+        load_s<VEC>(s_rs, col_off[0] * 4u, s_row, s[BUF]);
       }
       if (++ig == groups) {
         ig = 0;
@@ -293,7 +313,7 @@ struct WaveStream {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int i = 0; i < VEC / 4; ++i) {
-          const v4f x = *reinterpret_cast<const v4f *>(&s_lds[VEC * lane + 4 * i]);
+          const v4f x = *reinterpret_cast<const v4f *>(&s_lds[G::col(lane, 4 * i)]);
           sc[4 * i] = x.x;
           sc[4 * i + 1] = x.y;
           sc[4 * i + 2] = x.z;
@@ -311,12 +331,12 @@ struct WaveStream {
       // End of this tile's share of the run (or of the run): park the sums.
       if (++cg == groups || c0 + U == last_chunk) {
         cg = 0;
-        float *dst = slots + (size_t)cslot * (kWaves * MT * TW) + wave * (MT * TW) + lane_col;
+        float *dst = slots + (size_t)cslot * (kWaves * MT * TW) + wave * (MT * TW);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
           for (int v = 0; v < VEC; ++v) {
-            dst[m * TW + v] = acc[m][v];
+            dst[m * TW + G::col(lane, v)] = acc[m][v];
             acc[m][v] = 0.f;
           }
         ++cslot;
@@ -423,7 +443,6 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
   st.KB = p.KB;
   st.groups = p.groups;
   st.wave = wave;
-  st.lane_col = lane * VEC;
   st.pitch = p.pitch;
   st.a_lds = stage;
   st.slots = slots;
