@@ -109,6 +109,57 @@ q8_status q8_matvec_with_plan(const float *A, const int8_t *W, const float *S, f
                               void *stream);
 
 /*
+ * Fused matvec: sibling projections and the elementwise epilogue.
+ *
+ * "dot and tensor cores", section "The fused epilogue": a product that only
+ * feeds an elementwise statement is updated per element as it is written out
+ * instead of being stored and swept again (the page's examples scale a
+ * product, s = s * scale, and rescale an accumulator while adding a product,
+ * acc = acc * corr + dot(p, v)).  Here, for every sibling g:
+ *
+ *   C_g[m,n] = alpha * P_g[m,n] + corr[m] * C_g[m,n]     (corr != NULL)
+ *   C_g[m,n] = alpha * P_g[m,n]                          (corr == NULL)
+ *
+ * where P_g = A (x) dequant(W_g, S_g) is the Q8_0 matvec of q8_matvec.  Each
+ * output is rounded as fmaf(corr[m], C_old, alpha * P) (alpha * P alone
+ * without corr), so alpha == 1 with no corr reproduces q8_matvec's values.
+ *
+ * Siblings are up to Q8_MAX_SIBLINGS weight sets of the same shape that share
+ * the activation matrix A (for example the gate and up projections of an
+ * MLP, or q, k and v); they run in one launch, which streams every sibling's
+ * W and S once and stages A once per workgroup.
+ */
+#define Q8_MAX_SIBLINGS 4
+
+typedef struct q8_sibling {
+  const int8_t *W;  /* i8  [K, N], device */
+  const float *S;   /* f32 [ceil(K/32), N], device */
+  float *C;         /* f32 [M, N], device; read only when corr != NULL */
+} q8_sibling;
+
+typedef struct q8_epilogue {
+  float alpha;        /* scale of the product */
+  const float *corr;  /* f32 [M] device row factors of the existing C, or NULL */
+} q8_epilogue;
+
+/*
+ * q8_matvec_fused -- the siblings' matvecs with the epilogue, in one launch.
+ *   A         f32 [M, K], shared by all siblings
+ *   siblings  host array of n_siblings (1..Q8_MAX_SIBLINGS) descriptors; the
+ *             C arrays must be distinct and must not alias any input
+ *   epilogue  host pointer, or NULL for alpha = 1 and no corr
+ *   plan      as for q8_matvec_with_plan, or NULL for automatic; the
+ *             siblings' tiles form one list of n_siblings * ceil(N/(64*vec))
+ *             tiles, and W and S of every sibling must meet vec's alignment
+ * K == 0 gives a zero product (C = corr[m] * C, or zeros).  Deterministic.
+ * Errors: as q8_matvec; Q8_ERR_INVALID for n_siblings outside 1..4, a NULL
+ * siblings array or pointer, or an unsupported plan.
+ */
+q8_status q8_matvec_fused(const float *A, const q8_sibling *siblings, int32_t n_siblings,
+                          int64_t M, int64_t K, int64_t N, const q8_epilogue *epilogue,
+                          const q8_plan *plan, void *stream);
+
+/*
  * q8_dot_t -- C = A @ W^T in exact integer arithmetic.
  *   A  i8  [M, K]   row-major
  *   W  i8  [N, K]   row-major, one output row per row (K contiguous)

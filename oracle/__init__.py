@@ -18,7 +18,9 @@ Sources (Phobos documentation pages):
     loop is whole blocks plus one masked remainder.
   * "dot and tensor cores" (docs/language/dot-and-tensor-cores), the table of
     built-ins: dot_t(a, b) with a [M,K], b [N,K] computes a @ b^T; section
-    "Hardware paths": i8 operands accumulate in i32.
+    "Hardware paths": i8 operands accumulate in i32; section "The fused
+    epilogue": a product feeding an elementwise statement is updated as it is
+    written out (scale, and rescale-and-add).
 
 Every function is pinned by tests in ``tests/test_oracle.py`` against exact
 rational arithmetic, closed forms, library special cases and hand-derived
@@ -32,8 +34,11 @@ from .q8_oracle import (  # noqa: F401
     q8_matvec_per_weight,
     q8_normaliser,
     q8_matvec,
+    q8_epilogue,
+    q8_matvec_fused,
+    q8_fused_normaliser,
     normalised_error,
     dot_t,
     wrap_i32,
 )
-from .exact import q8_matvec_exact, dot_t_loops  # noqa: F401
+from .exact import q8_matvec_exact, q8_epilogue_exact, dot_t_loops  # noqa: F401

@@ -39,3 +39,20 @@ def dot_t_loops(A, W):
     A = np.asarray(A).astype(int).tolist()
     W = np.asarray(W).astype(int).tolist()
     return [[sum(x * y for x, y in zip(a_row, w_row)) for w_row in W] for a_row in A]
+
+
+def q8_epilogue_exact(A, W, S, alpha, corr=None, C_old=None):
+    """Exact alpha * C[m][n] + corr[m] * C_old[m][n] ("dot and tensor cores",
+    "The fused epilogue"), with C the exact Q8_0 matvec; nested Fractions."""
+    P = q8_matvec_exact(A, W, S)
+    al = Fraction(float(alpha))
+    out = []
+    for m, row in enumerate(P):
+        r = []
+        for n, p in enumerate(row):
+            y = al * p
+            if corr is not None:
+                y += Fraction(float(corr[m])) * Fraction(float(C_old[m][n]))
+            r.append(y)
+        out.append(r)
+    return out

@@ -131,6 +131,42 @@ def normalised_error(C_test, C_ref, D):
     return float(err.max())
 
 
+def q8_epilogue(P, alpha=1.0, corr=None, C_old=None):
+    """The fused epilogue of "dot and tensor cores" ("The fused epilogue"), f64.
+
+    A product that only feeds an elementwise statement is updated as it is
+    written out; the page's statements scale a product (s = s * scale) and
+    rescale an accumulator while adding a product (acc = acc * corr + dot).
+    Here y[m,n] = alpha * P[m,n] + corr[m] * C_old[m,n], or alpha * P[m,n]
+    without row factors.
+    """
+    y = float(alpha) * np.asarray(P, dtype=np.float64)
+    if corr is not None:
+        corr64 = np.asarray(corr, dtype=np.float64).reshape(-1, 1)
+        y = y + corr64 * np.asarray(C_old, dtype=np.float64)
+    return y
+
+
+def q8_matvec_fused(A, siblings, alpha=1.0, corr=None, C_olds=None):
+    """Sibling projections sharing A, each through the epilogue: for sibling g
+    with weights (W_g, S_g), q8_epilogue(q8_matvec(A, W_g, S_g), alpha, corr,
+    C_olds[g]).  Returns a list of f64 arrays [M, N]."""
+    out = []
+    for g, (W, S) in enumerate(siblings):
+        C_old = None if C_olds is None else C_olds[g]
+        out.append(q8_epilogue(q8_matvec(A, W, S), alpha, corr, C_old))
+    return out
+
+
+def q8_fused_normaliser(A, W, S, alpha=1.0, corr=None, C_old=None):
+    """|alpha| * D + |corr[m] * C_old[m,n]|: the sum of the magnitudes of the
+    terms of one fused output (D is q8_normaliser)."""
+    D = abs(float(alpha)) * q8_normaliser(A, W, S)
+    if corr is not None:
+        D = D + np.abs(np.asarray(corr, dtype=np.float64).reshape(-1, 1) * np.asarray(C_old, dtype=np.float64))
+    return D
+
+
 def wrap_i32(x):
     """Reduce integers modulo 2^32 into the int32 range (two's complement)."""
     x = np.asarray(x, dtype=np.int64)

@@ -19,12 +19,14 @@ Q8_ERR_UNSUPPORTED_DEVICE = 3
 Q8_ERR_HIP = 4
 
 BLOCK = 32
+MAX_SIBLINGS = 4
 
 #: Every symbol include/q8_gemv.h declares.
 EXPORTED = (
     "q8_matvec",
     "q8_matvec_with_plan",
     "q8_matvec_choose_plan",
+    "q8_matvec_fused",
     "q8_dot_t",
     "q8_status_string",
     "q8_last_hip_error",
@@ -38,6 +40,14 @@ class Q8Plan(ctypes.Structure):
 
     def as_dict(self):
         return {"vec": self.vec, "m_tile": self.m_tile, "workgroups": self.workgroups, "waves": self.waves}
+
+
+class Q8Sibling(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("S", ctypes.c_void_p), ("C", ctypes.c_void_p)]
+
+
+class Q8Epilogue(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_float), ("corr", ctypes.c_void_p)]
 
 
 class Q8Error(RuntimeError):
@@ -67,6 +77,9 @@ def load():
     L.q8_matvec_with_plan.restype = ctypes.c_int
     L.q8_matvec_choose_plan.argtypes = [i64, i64, i64, i64, i64, i32, ctypes.POINTER(Q8Plan)]
     L.q8_matvec_choose_plan.restype = ctypes.c_int
+    L.q8_matvec_fused.argtypes = [p, ctypes.POINTER(Q8Sibling), i32, i64, i64, i64,
+                                  ctypes.POINTER(Q8Epilogue), ctypes.POINTER(Q8Plan), p]
+    L.q8_matvec_fused.restype = ctypes.c_int
     L.q8_dot_t.argtypes = [p, p, p, i64, i64, i64, p]
     L.q8_dot_t.restype = ctypes.c_int
     L.q8_status_string.argtypes = [ctypes.c_int]
@@ -142,14 +155,54 @@ def q8_matvec(A, W, S, out=None, stream=None):
 def q8_matvec_with_plan(A, W, S, plan, out=None, stream=None):
     """q8_matvec with an explicit launch plan (dict with vec, m_tile, workgroups, waves)."""
     M, K, N, out = _q8_args(A, W, S, out)
-    pl = Q8Plan(int(plan.get("vec", 0)), int(plan.get("m_tile", 0)),
-                int(plan.get("workgroups", 0)), int(plan.get("waves", 0)))
+    pl = _plan_struct(plan)
     with torch.cuda.device(A.device):
         st = load().q8_matvec_with_plan(A.data_ptr(), W.data_ptr(), S.data_ptr(), out.data_ptr(),
                                         M, K, N, ctypes.byref(pl), _stream_handle(stream, A.device))
     if st != Q8_OK:
         raise Q8Error(st, "q8_matvec_with_plan")
     return out
+
+
+def _plan_struct(plan):
+    return Q8Plan(int(plan.get("vec", 0)), int(plan.get("m_tile", 0)),
+                  int(plan.get("workgroups", 0)), int(plan.get("waves", 0)))
+
+
+def q8_matvec_fused(A, Ws, Ss, outs=None, alpha=1.0, corr=None, plan=None, stream=None):
+    """Sibling projections sharing A, in one launch, through the epilogue
+    C_g = alpha * (A x dequant(W_g, S_g)) + corr[m] * C_g (corr: f32 [M] or
+    None).  With corr the existing contents of outs are read.  Returns the
+    list of C_g (f32 [M,N])."""
+    if not isinstance(Ws, (list, tuple)) or not isinstance(Ss, (list, tuple)) or len(Ws) != len(Ss):
+        raise ValueError("Ws and Ss must be lists of equal length")
+    n = len(Ws)
+    if not 1 <= n <= MAX_SIBLINGS:
+        raise ValueError(f"1..{MAX_SIBLINGS} siblings, got {n}")
+    if outs is None:
+        if corr is not None:
+            raise ValueError("corr reads the existing outputs: pass outs")
+        outs = [None] * n
+    if len(outs) != n:
+        raise ValueError("outs must have one entry per sibling")
+    res = []
+    M = K = N = None
+    for W, S, out in zip(Ws, Ss, outs):
+        M, K, N, out = _q8_args(A, W, S, out)
+        res.append(out)
+    if corr is not None:
+        _check_tensor("corr", corr, torch.float32, (M,))
+        if corr.device != A.device:
+            raise ValueError("all tensors must be on one device")
+    sib = (Q8Sibling * n)(*[Q8Sibling(W.data_ptr(), S.data_ptr(), C.data_ptr()) for W, S, C in zip(Ws, Ss, res)])
+    ep = Q8Epilogue(float(alpha), corr.data_ptr() if corr is not None else None)
+    pl = ctypes.byref(_plan_struct(plan)) if plan is not None else None
+    with torch.cuda.device(A.device):
+        st = load().q8_matvec_fused(A.data_ptr(), sib, n, M, K, N, ctypes.byref(ep), pl,
+                                    _stream_handle(stream, A.device))
+    if st != Q8_OK:
+        raise Q8Error(st, "q8_matvec_fused")
+    return res
 
 
 def q8_matvec_choose_plan(M, K, N, w_align=256, s_align=256, num_cus=256):

@@ -12,6 +12,7 @@
 namespace {
 
 using q8::kBlock;
+static_assert(q8::kMaxSiblings == Q8_MAX_SIBLINGS, "one sibling limit for the ABI and the kernel");
 
 thread_local int t_last_hip_error = 0;
 
@@ -85,10 +86,11 @@ bool vec_fits(int vec, int64_t N, int64_t w_align, int64_t s_align) {
   return N % vec == 0 && w_align % vec == 0 && s_align % s_need == 0;
 }
 
-// Launch layout derived from a plan: the (tile, group) units of W are dealt
-// in contiguous runs to n_wg workgroups per pass over W.
+// Launch layout derived from a plan: the (tile, group) units of the siblings'
+// W, sibling-major and tile-major, are dealt in contiguous runs to n_wg
+// workgroups per pass.
 struct Layout {
-  int64_t KB, G, n_tiles, m_chunks, units, n_wg, upw, rem, count_max, cmax;
+  int64_t KB, G, tiles_per, n_tiles, m_chunks, units, n_wg, upw, rem, count_max, cmax;
 };
 
 int64_t wg_of_unit(int64_t u, int64_t upw, int64_t rem) {
@@ -96,11 +98,12 @@ int64_t wg_of_unit(int64_t u, int64_t upw, int64_t rem) {
   return u < big ? u / (upw + 1) : rem + (u - big) / upw;
 }
 
-Layout make_layout(int64_t M, int64_t K, int64_t N, const q8_plan &pl, int64_t n_wg) {
+Layout make_layout(int64_t M, int64_t K, int64_t N, int64_t n_sib, const q8_plan &pl, int64_t n_wg) {
   Layout L;
   L.KB = ceil_div(K, kBlock);
   L.G = ceil_div(L.KB, q8::kWaves);
-  L.n_tiles = ceil_div(N, 64 * (int64_t)pl.vec);
+  L.tiles_per = ceil_div(N, 64 * (int64_t)pl.vec);
+  L.n_tiles = n_sib * L.tiles_per;
   L.m_chunks = ceil_div(M, pl.m_tile);
   L.units = L.n_tiles * L.G;
   L.n_wg = n_wg;
@@ -119,9 +122,9 @@ Layout make_layout(int64_t M, int64_t K, int64_t N, const q8_plan &pl, int64_t n
 
 // Fills in the workgroup count of a plan whose vec and m_tile are set.
 // Returns false if the plan cannot run.
-bool finish_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan *pl) {
+bool finish_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int32_t num_cus, q8_plan *pl) {
   const int64_t cap = q8::max_units_per_wg(pl->m_tile);
-  Layout L = make_layout(M, K, N, *pl, 1);
+  Layout L = make_layout(M, K, N, n_sib, *pl, 1);
   int64_t n_wg = pl->workgroups;
   if (n_wg == 0) {
     // Equal runs of units, at most one workgroup per CU (a workgroup holds
@@ -149,7 +152,7 @@ bool finish_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan *pl) 
     }
   }
   if (n_wg < 1 || n_wg > L.units) return false;
-  L = make_layout(M, K, N, *pl, n_wg);
+  L = make_layout(M, K, N, n_sib, *pl, n_wg);
   if (L.count_max > cap) return false;
   if (L.m_chunks * L.n_tiles * L.cmax * pl->m_tile * 64 * pl->vec >= kIndexLimit) return false;
   const int nseg = q8::max_segments((int)L.count_max, (int)L.G);
@@ -164,7 +167,7 @@ bool plan_is_valid_shape(int64_t M, int64_t K, int64_t N) {
   return M >= 0 && K >= 0 && N >= 0;
 }
 
-q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t w_align, int64_t s_align,
+q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w_align, int64_t s_align,
                        int32_t num_cus, const q8_plan *req, q8_plan *out) {
   q8_plan pl = req ? *req : q8_plan{0, 0, 0, 0};
   if (pl.waves != 0 && pl.waves != q8::kWaves) return Q8_ERR_INVALID;
@@ -184,7 +187,7 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t w_align, int64_t
   if (pl.vec != 16 && pl.vec != 8 && pl.vec != 4 && pl.vec != 2 && pl.vec != 1) return Q8_ERR_INVALID;
   if (pl.vec * pl.m_tile > 32 || !vec_fits(pl.vec, N, w_align, s_align)) return Q8_ERR_INVALID;
   if (pl.workgroups < 0) return Q8_ERR_INVALID;
-  if (K > 0 && !finish_plan(M, K, N, num_cus, &pl)) return Q8_ERR_INVALID;
+  if (K > 0 && !finish_plan(M, K, N, n_sib, num_cus, &pl)) return Q8_ERR_INVALID;
   *out = pl;
   return Q8_OK;
 }
@@ -224,14 +227,22 @@ q8_status get_workspace(int dev, hipStream_t stream, size_t partial_words, size_
   return Q8_OK;
 }
 
-q8_status matvec_impl(const float *A, const int8_t *W, const float *S, float *C, int64_t M,
-                      int64_t K, int64_t N, const q8_plan *req, void *stream_v) {
-  if (!plan_is_valid_shape(M, K, N)) return Q8_ERR_INVALID;
+// The fused matvec: every sibling's C = alpha * (A x dequant(W, S)) (+ corr[m] * C).
+q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64_t M, int64_t K, int64_t N,
+                     float alpha, const float *corr, const q8_plan *req, void *stream_v) {
+  if (!plan_is_valid_shape(M, K, N) || sib == nullptr || n_sib < 1 || n_sib > q8::kMaxSiblings)
+    return Q8_ERR_INVALID;
   if (M == 0 || N == 0) return Q8_OK;
   const int64_t KB = ceil_div(K, kBlock);
-  if ((M * K > 0 && A == nullptr) || (K * N > 0 && W == nullptr) || (KB * N > 0 && S == nullptr) ||
-      C == nullptr)
-    return Q8_ERR_INVALID;
+  if (M * K > 0 && A == nullptr) return Q8_ERR_INVALID;
+  int64_t w_align = 256, s_align = 256;
+  for (int64_t g = 0; g < n_sib; ++g) {
+    if ((K * N > 0 && sib[g].W == nullptr) || (KB * N > 0 && sib[g].S == nullptr) || sib[g].C == nullptr)
+      return Q8_ERR_INVALID;
+    const int64_t wa = address_alignment(sib[g].W), sa = address_alignment(sib[g].S);
+    if (wa < w_align) w_align = wa;
+    if (sa < s_align) s_align = sa;
+  }
   // Byte offsets into W and S are 32-bit (buffer descriptors), element offsets too.
   if (K * N >= kIndexLimit || M * K >= kIndexLimit || M * N >= kIndexLimit || 4 * KB * N >= kIndexLimit)
     return Q8_ERR_TOO_LARGE;
@@ -240,22 +251,33 @@ q8_status matvec_impl(const float *A, const int8_t *W, const float *S, float *C,
   DevInfo info;
   q8_status st = current_device(&dev, &info);
   if (st != Q8_OK) return st;
-  if (K == 0) return hip_status(q8::launch_zero_fill(C, (size_t)(M * N), stream));
+  if (K == 0) {
+    for (int64_t g = 0; g < n_sib; ++g) {
+      st = hip_status(q8::launch_empty_product(sib[g].C, (int)M, (int)N, alpha, corr, stream));
+      if (st != Q8_OK) return st;
+    }
+    return Q8_OK;
+  }
 
   q8_plan pl;
-  st = resolve_plan(M, K, N, address_alignment(W), address_alignment(S), info.cus, req, &pl);
+  st = resolve_plan(M, K, N, n_sib, w_align, s_align, info.cus, req, &pl);
   if (st != Q8_OK) return st;
 
-  const Layout L = make_layout(M, K, N, pl, pl.workgroups);
+  const Layout L = make_layout(M, K, N, n_sib, pl, pl.workgroups);
   q8::GemvArgs a;
   a.A = A;
-  a.W = W;
-  a.S = S;
-  a.C = C;
+  for (int g = 0; g < q8::kMaxSiblings; ++g) {
+    a.W[g] = g < n_sib ? sib[g].W : nullptr;
+    a.S[g] = g < n_sib ? sib[g].S : nullptr;
+    a.C[g] = g < n_sib ? sib[g].C : nullptr;
+  }
+  a.corr = corr;
+  a.alpha = alpha;
   a.M = (int)M;
   a.K = (int)K;
   a.N = (int)N;
   a.KB = (int)L.KB;
+  a.tiles_per = (int)L.tiles_per;
   a.n_tiles = (int)L.n_tiles;
   a.groups = (int)L.G;
   a.n_wg = (int)L.n_wg;
@@ -276,6 +298,12 @@ q8_status matvec_impl(const float *A, const int8_t *W, const float *S, float *C,
   return hip_status(q8::launch_gemv(pl.vec, pl.m_tile, a, (int)L.m_chunks, lds, stream));
 }
 
+q8_status matvec_impl(const float *A, const int8_t *W, const float *S, float *C, int64_t M,
+                      int64_t K, int64_t N, const q8_plan *req, void *stream) {
+  const q8_sibling one{W, S, C};
+  return fused_impl(A, &one, 1, M, K, N, 1.0f, nullptr, req, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,6 +320,14 @@ q8_status q8_matvec_with_plan(const float *A, const int8_t *W, const float *S, f
   return matvec_impl(A, W, S, C, M, K, N, plan, stream);
 }
 
+q8_status q8_matvec_fused(const float *A, const q8_sibling *siblings, int32_t n_siblings, int64_t M,
+                          int64_t K, int64_t N, const q8_epilogue *epilogue, const q8_plan *plan,
+                          void *stream) {
+  const float alpha = epilogue ? epilogue->alpha : 1.0f;
+  const float *corr = epilogue ? epilogue->corr : nullptr;
+  return fused_impl(A, siblings, n_siblings, M, K, N, alpha, corr, plan, stream);
+}
+
 q8_status q8_matvec_choose_plan(int64_t M, int64_t K, int64_t N, int64_t w_align,
                                 int64_t s_align, int32_t num_cus, q8_plan *out) {
   if (out == nullptr || num_cus < 1 || w_align < 1 || s_align < 1 || !plan_is_valid_shape(M, K, N))
@@ -299,7 +335,7 @@ q8_status q8_matvec_choose_plan(int64_t M, int64_t K, int64_t N, int64_t w_align
   if (M * K >= kIndexLimit || K * N >= kIndexLimit || M * N >= kIndexLimit ||
       4 * ceil_div(K, kBlock) * N >= kIndexLimit)
     return Q8_ERR_TOO_LARGE;
-  return resolve_plan(M, K, N, w_align, s_align, num_cus, nullptr, out);
+  return resolve_plan(M, K, N, 1, w_align, s_align, num_cus, nullptr, out);
 }
 
 q8_status q8_dot_t(const int8_t *A, const int8_t *W, int32_t *C, int64_t M, int64_t K, int64_t N,

@@ -23,23 +23,30 @@ __host__ __device__ constexpr int padded_pitch(int cols, int elem_bytes) {
   return (cols * elem_bytes) % kLdsBankPeriodBytes == 0 ? cols + 8 : cols;
 }
 
-// Arguments of the Q8_0 matvec kernel (one launch).  The (column tile,
-// 4-block group) units of W, tile-major, are dealt to the n_wg workgroups of a
-// pass in contiguous runs: upw units each, one more for the first rem.
+// Weight sets sharing one activation matrix in a single launch.
+constexpr int kMaxSiblings = 4;
+
+// Arguments of the Q8_0 matvec kernel (one launch).  The column tiles of all
+// siblings, sibling-major, form one list of n_tiles tiles; its (tile,
+// 4-block group) units, tile-major, are dealt to the n_wg workgroups of a pass
+// in contiguous runs: upw units each, one more for the first rem.
 struct GemvArgs {
-  const float *A;        // [M, K]
-  const int8_t *W;       // [K, N]
-  const float *S;        // [KB, N]
-  float *C;              // [M, N]
-  float *partial;        // [m_chunks][n_tiles][cmax][m_tile * 64 * vec] partial sums
-  uint32_t *counters;    // [m_chunks * n_tiles] arrival counters, zero between calls
+  const float *A;                 // [M, K]
+  const int8_t *W[kMaxSiblings];  // [K, N] per sibling
+  const float *S[kMaxSiblings];   // [KB, N] per sibling
+  float *C[kMaxSiblings];         // [M, N] per sibling
+  const float *corr;              // [M] epilogue row factors, or null
+  float alpha;                    // epilogue scale of the product
+  float *partial;                 // [m_chunks][n_tiles][cmax][m_tile * 64 * vec] partial sums
+  uint32_t *counters;             // [m_chunks * n_tiles] arrival counters, zero between calls
   int M, K, N, KB;
-  int n_tiles;           // column tiles of 64 * vec columns
-  int groups;            // groups of four K blocks per tile: ceil(KB / 4)
-  int n_wg;              // workgroups per pass (per chunk of m_tile rows of A)
-  int upw, rem;          // units per workgroup
-  int cmax;              // most workgroups that share one tile
-  int pitch;             // row pitch of a wave's activation stage in LDS, floats
+  int tiles_per;                  // column tiles of 64 * vec columns per sibling
+  int n_tiles;                    // tiles over all siblings
+  int groups;                     // groups of four K blocks per tile: ceil(KB / 4)
+  int n_wg;                       // workgroups per pass (per chunk of m_tile rows of A)
+  int upw, rem;                   // units per workgroup
+  int cmax;                       // most workgroups that share one tile
+  int pitch;                      // row pitch of a wave's activation stage in LDS, floats
 };
 
 // Launches the Q8_0 matvec kernel instance (vec, m_tile) on `stream`.
@@ -47,8 +54,12 @@ struct GemvArgs {
 hipError_t launch_gemv(int vec, int m_tile, const GemvArgs &args, int m_chunks,
                        size_t lds_bytes, hipStream_t stream);
 
-// Writes `n` zero words at `p` (used for K == 0 outputs and fresh counters).
+// Writes `n` zero words at `p` (used for fresh counters).
 hipError_t launch_zero_fill(void *p, size_t n_words, hipStream_t stream);
+
+// The epilogue with a zero product (K == 0): C[m,n] = alpha * 0 + corr[m] * C[m,n]
+// (corr null: the zero product alone).
+hipError_t launch_empty_product(float *C, int M, int N, float alpha, const float *corr, hipStream_t stream);
 
 // Largest dynamic LDS footprint (bytes) the matvec kernel may be given: a
 // gfx950 workgroup may use the CU's 160 KB; 1 KB stays for static LDS.

@@ -8,6 +8,15 @@ __global__ void zero_fill_kernel(uint32_t *p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
 
+__global__ void empty_product_kernel(float *C, int M, int N, float alpha, const float *corr) {
+  const size_t total = (size_t)M * N;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    float y = alpha * 0.f;
+    if (corr != nullptr) y = fmaf(corr[i / N], C[i], y);
+    C[i] = y;
+  }
+}
+
 GemvKernel pick(int vec, int m_tile) {
   switch (vec) {
     case 16: return gemv_kernel_v16(m_tile);
@@ -39,6 +48,15 @@ hipError_t launch_gemv(int vec, int m_tile, const GemvArgs &args, int m_chunks, 
     }
   }
   hipLaunchKernelGGL(k, dim3((unsigned)args.n_wg, (unsigned)m_chunks, 1), dim3(kThreads), lds_bytes, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_empty_product(float *C, int M, int N, float alpha, const float *corr, hipStream_t stream) {
+  const size_t total = (size_t)M * N;
+  if (total == 0) return hipSuccess;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(empty_product_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, M, N, alpha, corr);
   return hipGetLastError();
 }
 

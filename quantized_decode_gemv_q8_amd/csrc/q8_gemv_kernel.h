@@ -206,14 +206,16 @@ struct WaveStream {
   static constexpr int kUnroll = DEPTH / gcd_c(DEPTH, CPB) * CPB;
   static_assert(DEPTH >= 2, "at least one chunk in flight");
 
-  __amdgpu_buffer_rsrc_t w_rs, s_rs;
+  __amdgpu_buffer_rsrc_t w_rs, s_rs;  // descriptors of the sibling being issued
+  const GemvArgs *args;
   int K, N, KB, groups, wave, pitch, last_chunk;
   const float *a_lds;  // the wave's activation stage: [MT][pitch], block j at 32 j
   float *s_lds;        // the wave's scale hand-over area: 64 * VEC floats (VEC >= 8)
   int lane;
   uint32_t s_off[G::kScaleLoads];  // coalesced S column offsets for the block being issued
   float *slots;        // parked sums: slot q at slots + q * 4 * MT * TW (+ wave * MT * TW)
-  int it, ig;          // tile and group of the next block to issue
+  int it, ig;          // tile (over all siblings) and group of the next block to issue
+  int isib, itile;     // that tile's sibling and its tile within the sibling
   int cg, cslot;       // group of the block being used, next free slot
   uint32_t col_off[G::kPieces];  // lane byte offsets (per piece) into a W row for the block being issued
   int b_issue;         // that block
@@ -227,17 +229,19 @@ struct WaveStream {
   __device__ __forceinline__ void issue(int c0) {
     constexpr int BUF = U % kDepth, H = U % CPB;
     if constexpr (H == 0) {
+      w_rs = buffer_rsrc(args->W[isib], (uint32_t)K * (uint32_t)N);
+      s_rs = buffer_rsrc(args->S[isib], (uint32_t)KB * (uint32_t)N * 4u);
       // Columns past N (ragged last tile) load column 0 instead; blocks past
       // KB (in the last group of K) load row K-1 with zero activations.
 #pragma unroll
       for (int q = 0; q < G::kPieces; ++q) {
-        const int col = it * TW + G::col(lane, q * G::kPieceCols);
+        const int col = itile * TW + G::col(lane, q * G::kPieceCols);
         col_off[q] = col < N ? (uint32_t)col : 0u;
       }
       if constexpr (G::kSwizzleScales) {
 #pragma unroll
         for (int i = 0; i < G::kScaleLoads; ++i) {
-          const int c = it * TW + 256 * i + 4 * lane;
+          const int c = itile * TW + 256 * i + 4 * lane;
           s_off[i] = c < N ? (uint32_t)c * 4u : 0u;
         }
       }
@@ -267,6 +271,10 @@ struct WaveStream {
       if (++ig == groups) {
         ig = 0;
         ++it;
+        if (++itile == args->tiles_per) {
+          itile = 0;
+          ++isib;
+        }
       }
     }
   }
@@ -404,6 +412,18 @@ struct WaveStream {
 template <int VEC, int MT>
 constexpr int kStreamDepth = 4;
 
+// Writes output (row, n) of sibling `sib` through the epilogue of "dot and
+// tensor cores", section "The fused epilogue": the product x is updated per
+// element as it is written out, y = alpha * x + corr[row] * C[row, n] (the
+// second term only with row factors).  With alpha 1 and no row factors this
+// is a plain store of x.
+__device__ __forceinline__ void store_out(const GemvArgs &p, int sib, int row, int n, float x) {
+  float *c = p.C[sib] + (size_t)row * p.N + n;
+  float y = p.alpha * x;
+  if (p.corr != nullptr) y = fmaf(p.corr[row], *c, y);
+  *c = y;
+}
+
 // Workgroup that owns unit u when units are dealt in runs of upw (+1 for the
 // first rem workgroups).
 __device__ __forceinline__ int wg_of_unit(int u, int upw, int rem) {
@@ -436,8 +456,7 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
   __shared__ uint32_t last_mask;
 
   WaveStream<VEC, MT, kStreamDepth<VEC, MT>> st;
-  st.w_rs = buffer_rsrc(p.W, (uint32_t)p.K * (uint32_t)p.N);
-  st.s_rs = buffer_rsrc(p.S, (uint32_t)p.KB * (uint32_t)p.N * 4u);
+  st.args = &p;
   st.K = p.K;
   st.N = p.N;
   st.KB = p.KB;
@@ -449,6 +468,8 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
   st.s_lds = s_area + wave * 64 * VEC;
   st.lane = lane;
   st.it = t_first;
+  st.isib = t_first / p.tiles_per;
+  st.itile = t_first - st.isib * p.tiles_per;
   st.ig = g_first;
   st.cg = g_first;
   st.cslot = 0;
@@ -492,15 +513,16 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
     const int t = t_first + q;
     const int i0 = wg_of_unit(t * p.groups, p.upw, p.rem);
     const int i1 = wg_of_unit(t * p.groups + p.groups - 1, p.upw, p.rem);
+    const int sib = t / p.tiles_per;
     const float *sl = slots + (size_t)q * (kWaves * MT * TW);
     float *mine = p.partial + ((size_t)(mc * p.n_tiles + t) * p.cmax + (wg - i0)) * (MT * TW);
     any_partial |= i0 != i1;
     for (int o = tid; o < MT * TW; o += kThreads) {
       const float x = (sl[o] + sl[MT * TW + o]) + (sl[2 * MT * TW + o] + sl[3 * MT * TW + o]);
       const int m = o / TW;
-      const int n = t * TW + (o - m * TW);
+      const int n = (t - sib * p.tiles_per) * TW + (o - m * TW);
       if (i0 == i1) {
-        if (n < p.N && m0 + m < p.M) p.C[(size_t)(m0 + m) * p.N + n] = x;
+        if (n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, x);
       } else {
         // Device-coherent store (written through to the agent's coherence
         // point): no whole-cache write-back is needed to publish it.
@@ -570,12 +592,13 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
           total[jo] += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
         }
     }
+    const int sib = t / p.tiles_per;
 #pragma unroll
     for (int jo = 0; jo < OPT; ++jo) {
       const int o = tid + kThreads * jo;
       const int m = o / TW;
-      const int n = t * TW + (o - m * TW);
-      if (o < MT * TW && n < p.N && m0 + m < p.M) p.C[(size_t)(m0 + m) * p.N + n] = total[jo];
+      const int n = (t - sib * p.tiles_per) * TW + (o - m * TW);
+      if (o < MT * TW && n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, total[jo]);
     }
     if (tid == 0) __hip_atomic_store(&p.counters[mc * p.n_tiles + t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -21,7 +21,7 @@ BLOCK = 32  # Q8_0 block length along K
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str          # "q8" or "dot_t"
+    op: str          # "q8", "q8_fused" (siblings sharing A) or "dot_t"
     M: int
     K: int
     N: int
@@ -29,6 +29,7 @@ class Workload:
     w_dist: str      # "i8sym" (U{-127..127}) or "i8full" (U{-128..127})
     seed: tuple      # base seed; copy j uses seed + (j,) unless ``fixed_seed``
     fixed_seed: bool = False
+    siblings: int = 1  # weight sets sharing A ("q8_fused")
 
     @property
     def KB(self):
@@ -36,8 +37,9 @@ class Workload:
 
     def algorithmic_bytes(self):
         """Bytes the method must move once each (reads of A, W, S; write of C)."""
-        if self.op == "q8":
-            return self.K * self.N + 4 * self.KB * self.N + 4 * self.M * self.K + 4 * self.M * self.N
+        if self.op in ("q8", "q8_fused"):
+            per = self.K * self.N + 4 * self.KB * self.N + 4 * self.M * self.N
+            return self.siblings * per + 4 * self.M * self.K
         return self.M * self.K + self.N * self.K + 4 * self.M * self.N
 
 
@@ -51,6 +53,11 @@ WORKLOADS = {
     "mlp_down_28672x8192": Workload("mlp_down_28672x8192", "q8", 1, 28672, 8192, "normal", "i8sym", (3, 1)),
     # ragged batched case: 4 rows, K=4100 (last block 4 rows), N=5000
     "ragged_m4": Workload("ragged_m4", "q8", 4, 4100, 5000, "normal", "i8sym", (4, 0)),
+    # sibling projections sharing one activation row: an MLP's gate and up
+    # projections, and an attention block's q, k and v
+    "mlp_gate_up_8192x28672": Workload("mlp_gate_up_8192x28672", "q8_fused", 1, 8192, 28672, "normal", "i8sym",
+                                       (6, 0), siblings=2),
+    "attn_qkv_4096": Workload("attn_qkv_4096", "q8_fused", 1, 4096, 4096, "normal", "i8sym", (7, 0), siblings=3),
     # integer dot_t, weights stored one output row per row
     "dot_t_16x4096x4096": Workload("dot_t_16x4096x4096", "dot_t", 16, 4096, 4096, "i8full", "i8full", (5, 0)),
 }
@@ -83,6 +90,17 @@ def q8_inputs(M, K, N, seed, a_dist="normal", w_dist="i8sym"):
     return A, W, S
 
 
+def q8_fused_inputs(M, K, N, siblings, seed, a_dist="normal", w_dist="i8sym"):
+    """(A f32 [M,K], [W_g i8 [K,N]], [S_g f32 [ceil(K/32),N]]) drawn as A, W_0, S_0, W_1, S_1, ..."""
+    rng = rng_for(seed)
+    A = _draw(rng, a_dist, (M, K))
+    Ws, Ss = [], []
+    for _ in range(siblings):
+        Ws.append(_draw(rng, w_dist, (K, N)))
+        Ss.append(_draw(rng, "scale", ((K + BLOCK - 1) // BLOCK, N)))
+    return A, Ws, Ss
+
+
 def dot_t_inputs(M, K, N, seed, dist="i8full"):
     """(A i8 [M,K], W i8 [N,K]) drawn in that order."""
     rng = rng_for(seed)
@@ -99,4 +117,6 @@ def make(name, copy=0):
         if wl.fixed_seed:
             seed = wl.seed[0]
         return q8_inputs(wl.M, wl.K, wl.N, seed, wl.a_dist, wl.w_dist)
+    if wl.op == "q8_fused":
+        return q8_fused_inputs(wl.M, wl.K, wl.N, wl.siblings, seed, wl.a_dist, wl.w_dist)
     return dot_t_inputs(wl.M, wl.K, wl.N, seed, wl.a_dist)

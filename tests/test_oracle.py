@@ -347,3 +347,96 @@ def test_mutant_sign_of_masked_scale_is_caught():
     """Using |S| in the value (a sign slip) is caught by the exact pin with signed scales."""
     A, W, S = _rand_q8(1, 40, 4, seed=23, signed_s=True)
     assert not pin_exact(lambda a, w, s: oracle.q8_matvec(a, w, np.abs(s)), A, W, S)
+
+
+# ---------------------------------------------------------------- fused epilogue and siblings
+
+def _epilogue_fixture():
+    with open(os.path.join(GOLDEN, "q8_epilogue_hand_example.json")) as f:
+        g = json.load(f)
+    A, W, S, _, _ = hand_fixture_q8()
+    inp = g["inputs"]
+    corr = np.array(inp["corr"], np.float32)
+    C_old = np.array(inp["C_old"], np.float32)
+    return A, W, S, inp["alpha"], corr, C_old, np.array(g["expected_y"]), np.array(g["expected_D"])
+
+
+def pin_golden_epilogue(fn=None):
+    fn = fn or oracle.q8_epilogue
+    A, W, S, alpha, corr, C_old, y_exp, D_exp = _epilogue_fixture()
+    y = fn(oracle.q8_matvec(A, W, S), alpha, corr, C_old)
+    return np.array_equal(y, y_exp) and np.array_equal(oracle.q8_fused_normaliser(A, W, S, alpha, corr, C_old), D_exp)
+
+
+def pin_exact_epilogue(fn, A, W, S, alpha, corr, C_old):
+    """|fn - exact| <= (K + 64) * 2^-52 * D_fused elementwise."""
+    y = fn(oracle.q8_matvec(A, W, S), alpha, corr, C_old)
+    D = oracle.q8_fused_normaliser(A, W, S, alpha, corr, C_old)
+    ex = oracle.q8_epilogue_exact(A, W, S, alpha, corr, C_old)
+    K = A.shape[1]
+    for m in range(A.shape[0]):
+        for n in range(W.shape[1]):
+            if abs(Fraction(float(y[m, n])) - ex[m][n]) > Fraction((K + 64) * 2.0 ** -52) * Fraction(float(D[m, n])):
+                return False
+    return True
+
+
+def test_golden_epilogue_hand_example():
+    assert pin_golden_epilogue()
+
+
+@pytest.mark.parametrize("seed", [30, 31, 32])
+def test_epilogue_exact(seed):
+    rng = np.random.default_rng(seed)
+    A, W, S = _rand_q8(3, 70, 5, seed=seed, signed_s=True)
+    alpha = float(rng.choice([-3.0, 0.5, 1.0, 1.75]))
+    corr = rng.standard_normal(3).astype(np.float32)
+    C_old = rng.standard_normal((3, 5)).astype(np.float32)
+    assert pin_exact_epilogue(oracle.q8_epilogue, A, W, S, alpha, corr, C_old)
+
+
+def test_epilogue_special_cases():
+    A, W, S = _rand_q8(2, 100, 7, seed=33)
+    P = oracle.q8_matvec(A, W, S)
+    C_old = np.random.default_rng(34).standard_normal((2, 7)).astype(np.float32)
+    # alpha 1 without row factors is the plain product; alpha 0 keeps only corr * C_old
+    assert np.array_equal(oracle.q8_epilogue(P), P)
+    corr = np.array([0.5, -2.0], np.float32)
+    assert np.array_equal(oracle.q8_epilogue(P, 0.0, corr, C_old), corr[:, None].astype(np.float64) * C_old)
+    # zero row factors leave the scaled product
+    assert np.array_equal(oracle.q8_epilogue(P, 3.0, np.zeros(2, np.float32), C_old), 3.0 * P)
+
+
+def test_fused_siblings_are_independent_matvecs():
+    A, W0, S0 = _rand_q8(2, 300, 9, seed=35)
+    _, W1, S1 = _rand_q8(2, 300, 9, seed=36)
+    corr = np.array([1.5, -0.25], np.float32)
+    olds = [np.full((2, 9), 2.0, np.float32), np.full((2, 9), -1.0, np.float32)]
+    ys = oracle.q8_matvec_fused(A, [(W0, S0), (W1, S1)], 0.75, corr, olds)
+    assert len(ys) == 2
+    for (W, S), y, old in zip([(W0, S0), (W1, S1)], ys, olds):
+        assert np.array_equal(y, oracle.q8_epilogue(oracle.q8_matvec(A, W, S), 0.75, corr, old))
+
+
+def _mut_corr_by_column(P, alpha=1.0, corr=None, C_old=None):
+    y = float(alpha) * np.asarray(P, dtype=np.float64)
+    if corr is not None:
+        c = np.asarray(corr, dtype=np.float64)
+        y = y + np.resize(c, y.shape[1])[None, :] * np.asarray(C_old, dtype=np.float64)
+    return y
+
+
+def _mut_alpha_on_old(P, alpha=1.0, corr=None, C_old=None):
+    y = np.asarray(P, dtype=np.float64)
+    if corr is not None:
+        y = y + float(alpha) * np.asarray(corr, dtype=np.float64).reshape(-1, 1) * np.asarray(C_old, dtype=np.float64)
+    return y
+
+
+@pytest.mark.parametrize("mutant", [_mut_corr_by_column, _mut_alpha_on_old])
+def test_mutant_epilogue_is_caught(mutant):
+    rng = np.random.default_rng(37)
+    A, W, S = _rand_q8(3, 40, 4, seed=38)
+    corr = np.array([2.0, -1.0, 0.5], np.float32)
+    C_old = rng.standard_normal((3, 4)).astype(np.float32)
+    assert not (pin_golden_epilogue(mutant) and pin_exact_epilogue(mutant, A, W, S, 0.5, corr, C_old))
