@@ -42,7 +42,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 # Rotated copies per workload: enough to exceed the Infinity Cache (>= 1 GiB).
 COPIES = {"tiny": 1, "attn4096": 57, "mlp_up_8192x28672": 4, "mlp_down_28672x8192": 4,
-          "ragged_m4": 47, "dot_t_16x4096x4096": 63}
+          "ragged_m4": 47, "dot_t_16x4096x4096": 63, "mlp_gate_up_8192x28672": 2, "attn_qkv_4096": 19}
 
 
 def source_hash(paths):
@@ -240,6 +240,25 @@ def main():
         kernel_src = KERNEL_SRC
         used_plan = plan or binding.q8_matvec_choose_plan(wl.M, wl.K, wl.N, 256, 256,
                                                            torch.cuda.get_device_properties(dev).multi_processor_count)
+    elif wl.op == "q8_fused":
+        A0, W0s, S0s = host0
+        A = torch.from_numpy(A0).to(dev)
+        Ws, Ss = [], []
+        for j in range(n_copies):
+            _, Wjs, Sjs = host0 if j == 0 else workloads.make(wl.name, j)
+            Ws.append([torch.from_numpy(x).to(dev) for x in Wjs])
+            Ss.append([torch.from_numpy(x).to(dev) for x in Sjs])
+        Cs = [torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev) for _ in range(wl.siblings)]
+        C = Cs[0]
+
+        def launch(j):
+            binding.q8_matvec_fused(A, Ws[j], Ss[j], outs=Cs, plan=plan)
+
+        def launch_unfused(j):
+            for g in range(wl.siblings):
+                binding.q8_matvec(A, Ws[j][g], Ss[j][g], out=Cs[g])
+        kernel_src = KERNEL_SRC
+        used_plan = plan
     else:
         A0, W0 = host0
         A = torch.from_numpy(A0).to(dev)
@@ -258,12 +277,14 @@ def main():
         torch.cuda.synchronize()
         cols = np.unique(np.random.default_rng(0).integers(0, wl.N, 512))
         Cg = C.cpu().numpy()[:, cols]
-        if wl.op == "q8":
-            ref = oracle.q8_matvec(A0, np.ascontiguousarray(W0[:, cols]), np.ascontiguousarray(S0[:, cols]))
-            D = oracle.q8_normaliser(A0, np.ascontiguousarray(W0[:, cols]), np.ascontiguousarray(S0[:, cols]))
-            err = oracle.normalised_error(Cg, ref, D)
-            if not err <= 1e-5:
-                raise SystemExit(f"parity check failed: normalised error {err:.3e}")
+        if wl.op in ("q8", "q8_fused"):
+            pairs = [(W0, S0, Cg)] if wl.op == "q8" else \
+                [(W0s[g], S0s[g], Cs[g].cpu().numpy()[:, cols]) for g in range(wl.siblings)]
+            for Wg, Sg, Cgg in pairs:
+                Wc, Sc = np.ascontiguousarray(Wg[:, cols]), np.ascontiguousarray(Sg[:, cols])
+                err = oracle.normalised_error(Cgg, oracle.q8_matvec(A0, Wc, Sc), oracle.q8_normaliser(A0, Wc, Sc))
+                if not err <= 1e-5:
+                    raise SystemExit(f"parity check failed: normalised error {err:.3e}")
         else:
             if not np.array_equal(Cg, oracle.dot_t(A0, np.ascontiguousarray(W0[cols]))):
                 raise SystemExit("parity check failed: dot_t differs from the oracle")
@@ -293,6 +314,14 @@ def main():
           f"p10 {np.percentile(per, 10) * 1e3:.2f}, p90 {np.percentile(per, 90) * 1e3:.2f}",
           file=sys.stderr, flush=True)
 
+    unfused = None
+    if wl.op == "q8_fused":
+        wall_u, gpu_u = time_steps(launch_unfused, args.steps, args.warmup // 4, n_copies, torch)
+        unfused = {"launches_per_step": wl.siblings, "step_us_events": round(gpu_u * 1e6 / args.steps, 3),
+                   "value": round(nbytes * args.steps / wall_u / 1e9, 2)}
+        print(f"[bench] unfused (one q8_matvec per sibling): {gpu_u * 1e6 / args.steps:.2f} us/step",
+              file=sys.stderr, flush=True)
+
     traffic = measured_traffic(wl.name, kernel_src)
     headline = "Q8_0 GEMV effective HBM GB/s and % of peak at K=8192,N=28672, M=1"
     result = {
@@ -306,9 +335,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wl.op == "q8" else "i32",
+        "dtype": "i32" if wl.op == "dot_t" else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "rotated_copies": n_copies,
+        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "siblings": wl.siblings,
+                   "rotated_copies": n_copies,
                    "algorithmic_bytes_per_step": nbytes, "plan": used_plan},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
@@ -318,6 +348,8 @@ def main():
                       "p10": round(float(np.percentile(per, 10)) * 1e3, 3),
                       "p90": round(float(np.percentile(per, 90)) * 1e3, 3)},
     }
+    if unfused is not None:
+        result["unfused"] = unfused
     if not args.no_cpu_baseline and wl.op == "q8":
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, A0, W0, S0)

@@ -63,13 +63,16 @@ def test_plan_is_valid_and_normalised(M, K, N):
 
 
 def test_plan_vec_follows_shape_and_alignment():
-    assert plan(1, 4096, 4096)["vec"] == 8      # automatic plans use at most 8-byte lanes
-    assert plan(4, 4100, 5000)["vec"] == 8      # 5000 % 8 == 0, and 4 rows * 8 <= 32
+    assert plan(1, 8192, 28672)["vec"] == 8     # automatic plans use at most 8-byte lanes
+    assert plan(1, 4096, 4096)["vec"] == 4      # under 2 units per CU at vec 8: 4-byte lanes
+    assert plan(1, 4096, 4096, cus=64)["vec"] == 8
+    assert plan(4, 4100, 5000)["vec"] == 4      # 4 rows: vec * m_tile <= 16 (wider spills)
+    assert plan(2, 8192, 28672)["vec"] == 8     # 2 rows * 8 <= 16
     assert plan(1, 64, 4100)["vec"] == 4
     assert plan(1, 64, 4096, w_align=4)["vec"] == 4
     assert plan(1, 64, 4096, s_align=8)["vec"] == 2
     assert plan(1, 64, 7)["vec"] == 1
-    assert plan(8, 64, 4096)["vec"] == 4       # 8 rows: 8 * vec <= 32
+    assert plan(8, 64, 4096)["vec"] == 2        # 8 rows: 8 * vec <= 16
     assert plan(2, 64, 4096)["m_tile"] == 2
 
 
@@ -81,7 +84,7 @@ def test_plan_workgroups_fill_the_device():
         units = math.ceil(N / (64 * p["vec"])) * G
         assert units % p["workgroups"] == 0         # equal work for every workgroup at these shapes
         assert G % (units // p["workgroups"]) == 0  # and runs aligned with the tiles
-    assert plan(1, 4096, 4096)["workgroups"] == 256  # all 256 units, one each
+    assert plan(1, 4096, 4096)["workgroups"] == 256  # all 512 units at vec 4, two each
     small = plan(1, 8192, 28672, cus=8)
     assert small["workgroups"] == 16 * 2 or math.ceil(3584 / small["workgroups"]) <= 16
 
