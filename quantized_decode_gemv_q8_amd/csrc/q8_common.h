@@ -65,9 +65,13 @@ hipError_t launch_empty_product(float *C, int M, int N, float alpha, const float
 // gfx950 workgroup may use the CU's 160 KB; 1 KB stays for static LDS.
 constexpr size_t kMaxGemvLds = 159 * 1024;
 
+// Activation values each lane stages into its wave's LDS region (registers
+// per lane): m_tile * (blocks per wave in a run) * 32 <= 64 * kStageRegs.
+constexpr int kStageRegs = 8;
+
 // Most (tile, group) units one workgroup may take at a given m_tile: a wave
-// stages m_tile * units * 32 activations from 8 registers per lane.
-constexpr int max_units_per_wg(int m_tile) { return 64 * 8 / (m_tile * kBlock); }
+// stages m_tile * units * 32 activations from kStageRegs registers per lane.
+constexpr int max_units_per_wg(int m_tile) { return 64 * kStageRegs / (m_tile * kBlock); }
 
 // LDS bytes the matvec kernel needs: four private activation stages of
 // m_tile rows of `count` blocks, at vec >= 8 four scale hand-over areas of

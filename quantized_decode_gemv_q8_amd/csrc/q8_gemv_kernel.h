@@ -80,9 +80,6 @@ struct Geo {
   static constexpr int kScaleLoads = (VEC + 3) / 4;  // 16-byte S loads per lane and block
 };
 
-// Activation values each lane stages into its wave's LDS region:
-// m_tile * (blocks per wave and segment) * 32 <= 64 * kStageRegs.
-constexpr int kStageRegs = 8;
 
 // W and S are read with raw buffer loads: the lane's column byte offset is one
 // VGPR shared by every row, and the row's byte offset is a wave-uniform SGPR
