@@ -42,7 +42,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 # Rotated copies per workload: enough to exceed the Infinity Cache (>= 1 GiB).
 COPIES = {"tiny": 1, "attn4096": 57, "mlp_up_8192x28672": 4, "mlp_down_28672x8192": 4,
-          "ragged_m4": 47, "dot_t_16x4096x4096": 63, "mlp_gate_up_8192x28672": 2, "attn_qkv_4096": 19}
+          "ragged_m4": 47, "dot_t_16x4096x4096": 63, "mlp_gate_up_8192x28672": 2, "attn_qkv_4096": 19,
+          "batch16_8192x28672": 4}
 
 
 def source_hash(paths):
@@ -184,7 +185,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="mlp_up_8192x28672")
     ap.add_argument("--copies", type=int, default=0, help="rotated W/S copies (0: workload default)")
-    ap.add_argument("--plan", default="", help="vec,m_tile,workgroups override, e.g. 8,1,224")
+    ap.add_argument("--plan", default="", help="vec,m_tile,workgroups[,kind] override, e.g. 8,1,224 or 0,0,0,2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -216,8 +217,8 @@ def main():
 
     plan = None
     if args.plan:
-        v, mt, nwg = (int(x) for x in args.plan.split(","))
-        plan = {"vec": v, "m_tile": mt, "workgroups": nwg}
+        fields = [int(x) for x in args.plan.split(",")]
+        plan = dict(zip(("vec", "m_tile", "workgroups", "kind"), fields))
 
     # Inputs: copy j drawn with its own seed, uploaded once.
     host0 = workloads.make(wl.name, 0)

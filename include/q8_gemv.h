@@ -68,6 +68,10 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
 
 /*
  * Launch plan of q8_matvec.  Every field 0 means "choose automatically".
+ *   kind    Q8_PLAN_STREAM or Q8_PLAN_MATRIX (below); 0 picks one from the
+ *           shape (the matrix cores from Q8_MATRIX_MIN_ROWS rows on, when
+ *           allowed).
+ * For Q8_PLAN_STREAM, the per-row FMA stream:
  *   vec     columns (= bytes of W) each lane loads per row: 16, 8, 4, 2 or 1.
  *           N must be a multiple of vec, W 'vec'-byte aligned and S
  *           min(16, 4*vec)-byte aligned.
@@ -78,12 +82,25 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
  *           of equal length (within one), at most 16/m_tile units each.  A
  *           tile shared by several workgroups is combined in K order.
  *   waves   waves per workgroup; 4 is the only value supported.
+ * For Q8_PLAN_MATRIX, the matrix-core product of 2..32 rows ("dot and tensor
+ * cores", "Hardware paths"; A is split into three bf16 parts so that the
+ * result keeps f32 accuracy): it needs N % 16 == 0 and 16-byte aligned W and
+ * S, and serves q8_matvec and q8_matvec_with_plan (not the fused entry).
+ *   vec, m_tile  must be 0.
+ *   workgroups   tiles of 512 columns times K splits (a multiple of the tile
+ *           count; every split gets at least one 32-row block), or 0.
+ *   waves   4 or 0.
  */
+#define Q8_PLAN_STREAM 1
+#define Q8_PLAN_MATRIX 2
+#define Q8_MATRIX_MIN_ROWS 3
+#define Q8_MATRIX_MAX_ROWS 32
 typedef struct q8_plan {
   int32_t vec;
   int32_t m_tile;
   int32_t workgroups;
   int32_t waves;
+  int32_t kind;
 } q8_plan;
 
 /*

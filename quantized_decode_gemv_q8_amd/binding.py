@@ -20,6 +20,8 @@ Q8_ERR_HIP = 4
 
 BLOCK = 32
 MAX_SIBLINGS = 4
+PLAN_STREAM = 1
+PLAN_MATRIX = 2
 
 #: Every symbol include/q8_gemv.h declares.
 EXPORTED = (
@@ -36,10 +38,11 @@ EXPORTED = (
 
 class Q8Plan(ctypes.Structure):
     _fields_ = [("vec", ctypes.c_int32), ("m_tile", ctypes.c_int32),
-                ("workgroups", ctypes.c_int32), ("waves", ctypes.c_int32)]
+                ("workgroups", ctypes.c_int32), ("waves", ctypes.c_int32), ("kind", ctypes.c_int32)]
 
     def as_dict(self):
-        return {"vec": self.vec, "m_tile": self.m_tile, "workgroups": self.workgroups, "waves": self.waves}
+        return {"vec": self.vec, "m_tile": self.m_tile, "workgroups": self.workgroups, "waves": self.waves,
+                "kind": self.kind}
 
 
 class Q8Sibling(ctypes.Structure):
@@ -153,7 +156,7 @@ def q8_matvec(A, W, S, out=None, stream=None):
 
 
 def q8_matvec_with_plan(A, W, S, plan, out=None, stream=None):
-    """q8_matvec with an explicit launch plan (dict with vec, m_tile, workgroups, waves)."""
+    """q8_matvec with an explicit launch plan (dict with vec, m_tile, workgroups, waves, kind)."""
     M, K, N, out = _q8_args(A, W, S, out)
     pl = _plan_struct(plan)
     with torch.cuda.device(A.device):
@@ -166,7 +169,7 @@ def q8_matvec_with_plan(A, W, S, plan, out=None, stream=None):
 
 def _plan_struct(plan):
     return Q8Plan(int(plan.get("vec", 0)), int(plan.get("m_tile", 0)),
-                  int(plan.get("workgroups", 0)), int(plan.get("waves", 0)))
+                  int(plan.get("workgroups", 0)), int(plan.get("waves", 0)), int(plan.get("kind", 0)))
 
 
 def q8_matvec_fused(A, Ws, Ss, outs=None, alpha=1.0, corr=None, plan=None, stream=None):

@@ -30,7 +30,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // next 16 for a second, so each lane issues 32 contiguous bytes per chunk.
 // The i32 result of lane l is rows 4*(l/16) .. +3 of A's tile, column l % 16.
 constexpr int kChunkK = 128;
-constexpr int kMfmaUnroll = 4;  // chunks per wave kept in flight
+constexpr int kMfmaUnroll = 8;  // chunks per wave kept in flight (all of a wave's share at K = 4096)
 
 __device__ __forceinline__ v4i load16(const int8_t *p) { return *reinterpret_cast<const v4i *>(p); }
 

@@ -167,10 +167,56 @@ bool plan_is_valid_shape(int64_t M, int64_t K, int64_t N) {
   return M >= 0 && K >= 0 && N >= 0;
 }
 
+// Fills in a matrix-core plan: 512-column tiles times K splits.  Automatic
+// splits aim at two workgroups per CU for up to 16 rows (that instance's
+// registers leave room for two; its workgroups are bound by instruction
+// issue, so a second one per CU hides the first one's waits: 73.8 -> 66.6 us
+// at M=16, K=8192, N=28672) and one for up to 32 rows, at most 8 splits
+// (each split's partial is a whole 16*ceil(M/16) x 512 tile, read back by the
+// combine), and at most 64 blocks per split (the sequential sum over a
+// split's blocks stays short).
+bool finish_gemm_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan *pl) {
+  const int64_t n_tiles = ceil_div(N, q8::kGemmTileCols);
+  const int64_t KB = ceil_div(K, kBlock);
+  int64_t splits;
+  if (pl->workgroups == 0) {
+    splits = (M <= 16 ? 2 : 1) * (int64_t)num_cus / n_tiles;
+    if (splits > 8) splits = 8;
+    if (splits < ceil_div(KB, 64)) splits = ceil_div(KB, 64);
+    if (splits < 1) splits = 1;
+    if (splits > KB) splits = KB;
+    splits = ceil_div(KB, ceil_div(KB, splits));  // no empty split
+  } else {
+    if (pl->workgroups % n_tiles != 0) return false;
+    splits = pl->workgroups / n_tiles;
+    if (splits < 1 || splits > KB || ceil_div(KB, ceil_div(KB, splits)) != splits) return false;
+  }
+  const int64_t rows = 16 * ceil_div(M, 16);
+  if (n_tiles * splits * rows * q8::kGemmTileCols >= kIndexLimit) return false;
+  pl->workgroups = (int32_t)(n_tiles * splits);
+  pl->waves = q8::kWaves;
+  return true;
+}
+
+// matrix_ok: the call may use the matrix-core path (one weight set, plain
+// epilogue).
 q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w_align, int64_t s_align,
-                       int32_t num_cus, const q8_plan *req, q8_plan *out) {
-  q8_plan pl = req ? *req : q8_plan{0, 0, 0, 0};
+                       int32_t num_cus, bool matrix_ok, const q8_plan *req, q8_plan *out) {
+  q8_plan pl = req ? *req : q8_plan{0, 0, 0, 0, 0};
   if (pl.waves != 0 && pl.waves != q8::kWaves) return Q8_ERR_INVALID;
+  if (pl.kind != 0 && pl.kind != Q8_PLAN_STREAM && pl.kind != Q8_PLAN_MATRIX) return Q8_ERR_INVALID;
+  const bool matrix_fits = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 && N % 16 == 0 &&
+                           w_align % 16 == 0 && s_align % 16 == 0;
+  if (pl.kind == 0)
+    pl.kind = (matrix_fits && M >= Q8_MATRIX_MIN_ROWS && pl.vec == 0 && pl.m_tile == 0 && pl.workgroups == 0)
+                  ? Q8_PLAN_MATRIX
+                  : Q8_PLAN_STREAM;
+  if (pl.kind == Q8_PLAN_MATRIX) {
+    if (!matrix_fits || pl.vec != 0 || pl.m_tile != 0 || pl.workgroups < 0) return Q8_ERR_INVALID;
+    if (!finish_gemm_plan(M, K, N, num_cus, &pl)) return Q8_ERR_INVALID;
+    *out = pl;
+    return Q8_OK;
+  }
   if (pl.m_tile == 0) pl.m_tile = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
   if (pl.m_tile != 1 && pl.m_tile != 2 && pl.m_tile != 4 && pl.m_tile != 8) return Q8_ERR_INVALID;
   if (pl.vec == 0) {
@@ -197,6 +243,7 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   if (pl.vec * pl.m_tile > 32 || !vec_fits(pl.vec, N, w_align, s_align)) return Q8_ERR_INVALID;
   if (pl.workgroups < 0) return Q8_ERR_INVALID;
   if (K > 0 && !finish_plan(M, K, N, n_sib, num_cus, &pl)) return Q8_ERR_INVALID;
+  pl.kind = Q8_PLAN_STREAM;
   *out = pl;
   return Q8_OK;
 }
@@ -269,8 +316,31 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
   }
 
   q8_plan pl;
-  st = resolve_plan(M, K, N, n_sib, w_align, s_align, info.cus, req, &pl);
+  const bool plain = n_sib == 1 && alpha == 1.0f && corr == nullptr;
+  st = resolve_plan(M, K, N, n_sib, w_align, s_align, info.cus, plain, req, &pl);
   if (st != Q8_OK) return st;
+
+  if (pl.kind == Q8_PLAN_MATRIX) {
+    q8::GemmArgs g;
+    g.A = A;
+    g.W = sib[0].W;
+    g.S = sib[0].S;
+    g.C = sib[0].C;
+    g.M = (int)M;
+    g.K = (int)K;
+    g.N = (int)N;
+    g.KB = (int)KB;
+    g.n_tiles = (int)ceil_div(N, q8::kGemmTileCols);
+    g.splits = pl.workgroups / g.n_tiles;
+    g.bps = (int)ceil_div(KB, g.splits);
+    Workspace ws;
+    const size_t part = g.splits > 1 ? (size_t)g.n_tiles * g.splits * 16 * ceil_div(M, 16) * q8::kGemmTileCols : 1;
+    st = get_workspace(dev, stream, part, (size_t)g.n_tiles, &ws);
+    if (st != Q8_OK) return st;
+    g.partial = ws.partial;
+    g.counters = ws.counters;
+    return hip_status(q8::launch_gemm(g, stream));
+  }
 
   const Layout L = make_layout(M, K, N, n_sib, pl, pl.workgroups);
   q8::GemvArgs a;
@@ -344,7 +414,7 @@ q8_status q8_matvec_choose_plan(int64_t M, int64_t K, int64_t N, int64_t w_align
   if (M * K >= kIndexLimit || K * N >= kIndexLimit || M * N >= kIndexLimit ||
       4 * ceil_div(K, kBlock) * N >= kIndexLimit)
     return Q8_ERR_TOO_LARGE;
-  return resolve_plan(M, K, N, 1, w_align, s_align, num_cus, nullptr, out);
+  return resolve_plan(M, K, N, 1, w_align, s_align, num_cus, true, nullptr, out);
 }
 
 q8_status q8_dot_t(const int8_t *A, const int8_t *W, int32_t *C, int64_t M, int64_t K, int64_t N,

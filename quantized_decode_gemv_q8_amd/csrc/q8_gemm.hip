@@ -1,0 +1,383 @@
+// Q8_0 product for a few activation rows (2 <= M <= 32) on the matrix cores:
+// C[m,n] = sum_k A[m,k] * W[k,n] * S[k/32, n], reading W and S once for all
+// rows.
+//
+// Operation: "Q8_0 matvec" page, sections "The tensors" (definition),
+// "Factoring out the scale" (the scale multiplies each block's unscaled
+// partial once per block and column) and "Bounds" (ragged N and K are
+// masked).  At M rows the per-row FMA path costs M multiply-adds per weight
+// and runs out of vector ALU well before HBM bandwidth; here the contraction
+// goes to v_mfma_f32_16x16x32_bf16, whose k-slice of 32 is exactly one Q8_0
+// block, so the block's unscaled partial comes out of the matrix core and is
+// scaled once per block and column, as the page prescribes.
+//
+// Precision.  "dot and tensor cores" (section "Hardware paths") notes that
+// tensor-core f32 paths round their operands to 16 bits; that alone would
+// miss a 1e-5 relative bound.  W is exact in bf16 (|w| <= 128 has at most 8
+// significant bits).  A is split exactly into three bf16 parts,
+// a = hi + mid + lo + r with |r| <= 2^-24 |a| (each part takes the rounding
+// of the remainder so far; every subtraction is exact in f32), and every
+// block takes three MFMAs, one per part, into the same f32 accumulator.
+//
+// Work decomposition:
+//   * A workgroup (four wave64s) owns a tile of 512 columns and a contiguous
+//     range of K blocks (a split); the splits of a tile are combined as in the
+//     matvec: device-coherent partials, an arrival counter, and the last
+//     arrival sums the splits in K order.
+//   * Per block the workgroup loads W[32 rows, 512 columns] with 16-byte
+//     loads (a wave instruction reads two whole 512-byte row segments) into
+//     LDS, several blocks ahead in registers.  A's block (M x 32) is split
+//     into its three bf16 parts in LDS once per workgroup.
+//   * Wave w computes columns [128w, 128w + 128) as eight 16x16 output tiles
+//     per 16 rows of A.  For the B operand a lane needs eight consecutive k of
+//     one column; it reads four columns x eight rows as dwords from LDS and
+//     converts the bytes straight into bf16 pairs in k order (a byte-selecting
+//     convert and a byte permute), so the transpose costs nothing extra.
+//     Lane l of tile i of column group q supplies column 64q + 4(l%16) + i,
+//     which is the column its outputs belong to.
+#include <type_traits>
+
+#include "q8_common.h"
+
+namespace q8 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGemmCols = kGemmTileCols;   // columns per workgroup tile
+constexpr int kWaveCols = 128;             // columns per wave
+constexpr int kWPitch = kGemmCols + 16;    // LDS row pitch of a W block, bytes (16-byte aligned rows)
+constexpr int kAPitch = 40;                // LDS row pitch of an A block part, bf16 (80 bytes)
+constexpr int kDepthG = 3;                 // W blocks held in registers ahead of the one in LDS
+constexpr int kStreamPolicyG = 2;          // non-temporal: W and S are read once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Round-to-nearest-even f32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Two signed bytes (byte `i` of words x0 and x1) as a pair of bf16 in one
+// dword, x0's in the low half.  Exact: the f32 of a byte has 16 zero low bits.
+__device__ __forceinline__ uint32_t byte_pair_bf16(uint32_t x0, uint32_t x1, int i) {
+  const float f0 = static_cast<float>(static_cast<int8_t>(x0 >> (8 * i)));
+  const float f1 = static_cast<float>(static_cast<int8_t>(x1 >> (8 * i)));
+  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+// Makes this workgroup's LDS writes visible to its other waves without
+// waiting for outstanding global loads (a plain __syncthreads would drain the
+// prefetch ring every block).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int B, int E>
+struct SFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F &&f) {
+    if constexpr (B < E) {
+      f(std::integral_constant<int, B>{});
+      SFor<B + 1, E>::run(f);
+    }
+  }
+};
+
+// RT: 16-row tiles of A (M <= 16 * RT).
+template <int RT>
+__global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) int8_t w_lds[kBlock * kWPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t a_lds[3][16 * RT * kAPitch];
+  __shared__ uint32_t last_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = blockIdx.x;
+  const int split = blockIdx.y;
+  const int n0 = tile * kGemmCols;
+  const int b_begin = split * p.bps;
+  const int b_end = min(p.KB, b_begin + p.bps);
+  const int nb = b_end - b_begin;  // >= 1 (the host never launches an empty split)
+
+  // Every prefetch is issued unconditionally (a conditional load makes the
+  // compiler wait for all outstanding loads); the ones past this split's last
+  // block go through descriptors with no records, which return zeros without
+  // touching memory.
+  const uint32_t w_bytes = (uint32_t)p.K * (uint32_t)p.N;
+  const uint32_t s_bytes = (uint32_t)p.KB * (uint32_t)p.N * 4u;
+  const uint32_t a_bytes = (uint32_t)p.M * (uint32_t)p.K * 4u;
+
+  // This thread's 16-byte piece of a W block: row 8*wave + 2*i + lane/32,
+  // columns n0 + 16*(lane%32) .. +15, for i = 0..3.  The row pair's first
+  // row goes into the wave-uniform scalar offset, clamped to K - 1; the
+  // second is a per-lane step of one row, taken only while that row exists.
+  // Columns past N (the ragged last tile; N is a multiple of 16) read column
+  // 0, rows past K re-read a row of W; their activations are zero.
+  const int wcol = n0 + 16 * (lane & 31);
+  const uint32_t w_voff = wcol < p.N ? (uint32_t)wcol : 0u;
+  const bool upper = (lane >> 5) != 0;
+  auto load_w = [&](int b, bool live, u4 (&x)[4]) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(p.W, live ? w_bytes : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = min(b * kBlock + 8 * wave + 2 * i, p.K - 1);
+      const uint32_t voff = w_voff + (upper && r + 1 < p.K ? (uint32_t)p.N : 0u);
+      x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (uint32_t)r * (uint32_t)p.N, kStreamPolicyG);
+    }
+  };
+
+  // Scales of this lane's output columns: group q of the wave, columns
+  // 64q + 4(l%16) .. +3 of the wave's 128.
+  const int c16 = lane & 15;
+  const int g4 = lane >> 4;
+  uint32_t s_voff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = n0 + kWaveCols * wave + 64 * q + 4 * c16;
+    s_voff[q] = c < p.N ? (uint32_t)c * 4u : 0u;
+  }
+
+  // Activation block b: elements e = tid + 256 j of the 16*RT x 32 block.
+  constexpr int kAElems = 16 * RT * kBlock / kThreads;  // per thread
+  // Elements past M or K load element 0; they are replaced by zero when the
+  // block is staged (not here, which would wait for the load at once).
+  auto a_ok = [&](int b, int j) {
+    const int e = tid + kThreads * j;
+    return (e >> 5) < p.M && b * kBlock + (e & 31) < p.K;
+  };
+  auto load_a = [&](int b, bool live, float (&v)[kAElems]) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(p.A, live ? a_bytes : 0u);
+#pragma unroll
+    for (int j = 0; j < kAElems; ++j) {
+      const int e = tid + kThreads * j;
+      const uint32_t off = a_ok(b, j) ? ((uint32_t)(e >> 5) * (uint32_t)p.K + (uint32_t)(b * kBlock + (e & 31))) * 4u : 0u;
+      v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0u, 0));
+    }
+  };
+
+  f4 acc[8][RT];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[t][r] = f4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_s = [&](int b, bool live, u4 (&sv)[2]) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(p.S, live ? s_bytes : 0u);
+    const uint32_t soff = (uint32_t)min(b, p.KB - 1) * (uint32_t)p.N * 4u;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) sv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, s_voff[q], soff, kStreamPolicyG);
+  };
+
+  // Register ring: W, A and S of blocks b_begin + j for j < kDepthG are in flight.
+  u4 wring[kDepthG][4];
+  float aring[kDepthG][kAElems];
+  u4 sring[kDepthG][2];
+#pragma unroll
+  for (int d = 0; d < kDepthG; ++d) {
+    load_w(b_begin + d, d < nb, wring[d]);
+    load_a(b_begin + d, d < nb, aring[d]);
+    load_s(b_begin + d, d < nb, sring[d]);
+  }
+
+  // Block j from ring slot D: stage it in LDS, refill the slot, multiply.
+  auto process = [&](auto d_, auto refill_, int j) {
+    constexpr int D = decltype(d_)::value;
+    constexpr bool REFILL = decltype(refill_)::value;
+      const int b = b_begin + j;
+      // Scales of this block for the lane's eight output columns.
+      const u4 (&sv)[2] = sring[D];
+      // Block j into LDS (after every wave has finished with block j - 1).
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * wave + 2 * i + (lane >> 5);
+        *reinterpret_cast<u4 *>(&w_lds[row * kWPitch + 16 * (lane & 31)]) = wring[D][i];
+      }
+#pragma unroll
+      for (int jj = 0; jj < kAElems; ++jj) {
+        const int e = tid + kThreads * jj;
+        const int m = e >> 5;
+        const int k = e & 31;
+        const float a = a_ok(b, jj) ? aring[D][jj] : 0.f;
+        const uint32_t hi = bf16_bits(a);
+        const float r1 = a - bf16_value(hi);
+        const uint32_t mid = bf16_bits(r1);
+        const float r2 = r1 - bf16_value(mid);
+        a_lds[0][m * kAPitch + k] = (uint16_t)hi;
+        a_lds[1][m * kAPitch + k] = (uint16_t)mid;
+        a_lds[2][m * kAPitch + k] = (uint16_t)bf16_bits(r2);
+      }
+      lds_barrier();
+      // Refill this ring slot with block j + kDepthG (past the split's end:
+      // loads that return zeros, issued anyway to keep the pattern fixed).
+      if constexpr (REFILL) {
+        load_w(b + kDepthG, j + kDepthG < nb, wring[D]);
+        load_a(b + kDepthG, j + kDepthG < nb, aring[D]);
+      }
+      // A operands: row 16r + l%16, k = 8*(l/16) .. +7, for each part.
+      bf16x8 aop[3][RT];
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          aop[part][r] = *reinterpret_cast<const bf16x8 *>(&a_lds[part][(16 * r + c16) * kAPitch + 8 * g4]);
+      // B operands of the wave's eight column tiles: four columns x eight
+      // rows of W per lane and column group, as bf16 pairs in k order.
+      bf16x8 bop[8];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        uint32_t x[8];
+        const int cb = kWaveCols * wave + 64 * q + 4 * c16;
+#pragma unroll
+        for (int jr = 0; jr < 8; ++jr) x[jr] = *reinterpret_cast<const uint32_t *>(&w_lds[(8 * g4 + jr) * kWPitch + cb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u4 bw;
+          bw.x = byte_pair_bf16(x[0], x[1], i);
+          bw.y = byte_pair_bf16(x[2], x[3], i);
+          bw.z = byte_pair_bf16(x[4], x[5], i);
+          bw.w = byte_pair_bf16(x[6], x[7], i);
+          bop[4 * q + i] = __builtin_bit_cast(bf16x8, bw);
+        }
+      }
+      // The block's unscaled partial of every tile: one MFMA per part of A,
+      // part-major so that consecutive MFMAs are independent.
+      f4 part[8][RT];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) part[t][r] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pa = 0; pa < 3; ++pa)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int r = 0; r < RT; ++r)
+            part[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[pa][r], bop[t], part[t][r], 0, 0, 0);
+      // "Factoring out the scale": one multiply per block and column.
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float s = reinterpret_cast<const float *>(&sv[t >> 2])[t & 3];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[t][r] = f4{fmaf(part[t][r].x, s, acc[t][r].x), fmaf(part[t][r].y, s, acc[t][r].y),
+                         fmaf(part[t][r].z, s, acc[t][r].z), fmaf(part[t][r].w, s, acc[t][r].w)};
+      }
+    // The scales were used above: refill their slot now.
+    if constexpr (REFILL) load_s(b + kDepthG, j + kDepthG < nb, sring[D]);
+  };
+
+  // Whole rounds of kDepthG blocks with a fixed load pattern, then the last
+  // nb % kDepthG blocks from the ring without refills.
+  const int rounds = nb / kDepthG;
+  for (int r = 0; r < rounds; ++r) {
+    SFor<0, kDepthG>::run([&](auto d_) { process(d_, std::true_type{}, r * kDepthG + decltype(d_)::value); });
+  }
+  const int tail = nb - rounds * kDepthG;
+  SFor<0, kDepthG - 1>::run([&](auto d_) {
+    if (decltype(d_)::value < tail) process(d_, std::false_type{}, rounds * kDepthG + decltype(d_)::value);
+  });
+
+  // Lane l of tile (q, i) holds rows 16r + 4(l/16) .. +3 of column
+  // 64q + 4(l%16) + i of the wave's 128.
+  auto out_index = [&](int t, int r, int e, int &m, int &col) {
+    const int q = t >> 2, i = t & 3;
+    m = 16 * r + 4 * g4 + e;
+    col = kWaveCols * wave + 64 * q + 4 * c16 + i;
+  };
+  if (p.splits == 1) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int m, col;
+          out_index(t, r, e, m, col);
+          if (m < p.M && n0 + col < p.N) p.C[(size_t)m * p.N + n0 + col] = acc[t][r][e];
+        }
+    return;
+  }
+
+  // Split-K: publish this split's partial [16 RT][512] with device-coherent
+  // stores, count it, and let the last split of the tile sum them in K order.
+  constexpr int kTileElems = 16 * RT * kGemmCols;
+  float *mine = p.partial + ((size_t)tile * p.splits + split) * kTileElems;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int m, col;
+        out_index(t, r, e, m, col);
+        __hip_atomic_store(&mine[m * kGemmCols + col], acc[t][r][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = prev == (uint32_t)(p.splits - 1);
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  // Sum the splits in K order: pairwise over groups of eight, then the groups
+  // in order (the same tree as the matvec's combine).  Each thread owns
+  // outputs tid + 256 i; they are summed eight at a time, with every load of a
+  // batch in flight together.
+  const float *src = p.partial + (size_t)tile * p.splits * kTileElems;
+  constexpr int kOut = kTileElems / kThreads;
+  constexpr int kBatch = 8;
+  for (int i0 = 0; i0 < kOut; i0 += kBatch) {
+    float total[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) total[i] = 0.f;
+    for (int c = 0; c < p.splits; c += 8) {
+      float v[kBatch][8];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          v[i][s] = c + s < p.splits ? __hip_atomic_load(&src[(size_t)(c + s) * kTileElems + tid + kThreads * (i0 + i)],
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                     : 0.f;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        total[i] += ((v[i][0] + v[i][1]) + (v[i][2] + v[i][3])) + ((v[i][4] + v[i][5]) + (v[i][6] + v[i][7]));
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int o = tid + kThreads * (i0 + i);
+      const int m = o / kGemmCols;
+      const int col = o - m * kGemmCols;
+      if (m < p.M && n0 + col < p.N) p.C[(size_t)m * p.N + n0 + col] = total[i];
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.n_tiles, (unsigned)a.splits);
+  if (a.M <= 16) {
+    hipLaunchKernelGGL(q8_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, a);
+  } else if (a.M <= 32) {
+    hipLaunchKernelGGL(q8_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace q8

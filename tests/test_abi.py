@@ -53,6 +53,15 @@ def plan(M, K, N, w_align=256, s_align=256, cus=256):
 def test_plan_is_valid_and_normalised(M, K, N):
     p = plan(M, K, N)
     KB = math.ceil(K / 32)
+    if p["kind"] == binding.PLAN_MATRIX:
+        # matrix cores: 3..32 rows, N a multiple of 16, 512-column tiles x K splits
+        assert 3 <= M <= 32 and N % 16 == 0 and p["vec"] == 0 and p["m_tile"] == 0 and p["waves"] == 4
+        tiles = math.ceil(N / 512)
+        assert p["workgroups"] % tiles == 0
+        splits = p["workgroups"] // tiles
+        assert 1 <= splits <= KB and math.ceil(KB / math.ceil(KB / splits)) == splits
+        return
+    assert p["kind"] == binding.PLAN_STREAM
     assert p["vec"] in (16, 8, 4, 2, 1) and N % p["vec"] == 0
     assert p["m_tile"] in (1, 2, 4, 8) and p["m_tile"] * p["vec"] <= 32
     assert p["waves"] == 4
@@ -66,14 +75,27 @@ def test_plan_vec_follows_shape_and_alignment():
     assert plan(1, 8192, 28672)["vec"] == 8     # automatic plans use at most 8-byte lanes
     assert plan(1, 4096, 4096)["vec"] == 4      # under 2 units per CU at vec 8: 4-byte lanes
     assert plan(1, 4096, 4096, cus=64)["vec"] == 8
-    assert plan(4, 4100, 5000)["vec"] == 4      # 4 rows: vec * m_tile <= 16 (wider spills)
+    assert plan(4, 4100, 5000)["vec"] == 4      # 4 rows on the stream (N % 16 != 0): vec * m_tile <= 16
     assert plan(2, 8192, 28672)["vec"] == 8     # 2 rows * 8 <= 16
     assert plan(1, 64, 4100)["vec"] == 4
     assert plan(1, 64, 4096, w_align=4)["vec"] == 4
     assert plan(1, 64, 4096, s_align=8)["vec"] == 2
     assert plan(1, 64, 7)["vec"] == 1
-    assert plan(8, 64, 4096)["vec"] == 2        # 8 rows: 8 * vec <= 16
+    assert plan(8, 64, 4100)["vec"] == 2        # 8 rows on the stream (N % 16 != 0): 8 * vec <= 16
     assert plan(2, 64, 4096)["m_tile"] == 2
+
+
+def test_plan_kind_follows_rows_and_layout():
+    assert plan(1, 8192, 28672)["kind"] == binding.PLAN_STREAM
+    assert plan(2, 8192, 28672)["kind"] == binding.PLAN_STREAM     # below the matrix-core row count
+    assert plan(3, 8192, 28672)["kind"] == binding.PLAN_MATRIX
+    assert plan(32, 8192, 28672)["kind"] == binding.PLAN_MATRIX
+    assert plan(33, 8192, 28672)["kind"] == binding.PLAN_STREAM    # above it
+    assert plan(16, 8192, 5000)["kind"] == binding.PLAN_STREAM     # N % 16 != 0
+    assert plan(16, 8192, 4096, w_align=8)["kind"] == binding.PLAN_STREAM
+    assert plan(16, 8192, 28672)["workgroups"] == 56 * 8          # two workgroups per CU up to 16 rows
+    assert plan(32, 8192, 28672)["workgroups"] == 56 * 4          # one above
+    assert plan(16, 28672, 28672)["workgroups"] == 56 * 14       # at most 64 blocks per split
 
 
 def test_plan_workgroups_fill_the_device():
