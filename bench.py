@@ -38,6 +38,9 @@ CSRC = os.path.join(ROOT, "quantized_decode_gemv_q8_amd", "csrc")
 # Sources whose hash stamps a traffic measurement (the kernel code itself).
 KERNEL_SRC = (os.path.join(CSRC, "q8_gemv_kernel.h"), os.path.join(CSRC, "q8_common.h"))
 DOT_SRC = (os.path.join(CSRC, "dot_t.hip"), os.path.join(CSRC, "q8_common.h"))
+GEMM_SRC = (os.path.join(CSRC, "q8_gemm.hip"), os.path.join(CSRC, "q8_common.h"))
+# Kernel-name prefix of each source set, as rocprofv3 reports it.
+KERNEL_NAMES = {KERNEL_SRC: "q8_gemv_kernel", GEMM_SRC: "q8_gemm_kernel", DOT_SRC: "dot_t_"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 # Rotated copies per workload: enough to exceed the Infinity Cache (>= 1 GiB).
@@ -158,7 +161,7 @@ def ingest_pmc(fetch_csv, write_csv, workload, kernel_path):
             raise SystemExit(f"no kernel matching {sub!r} in {sorted(d)}")
         return hits[0]
 
-    kname = "q8_gemv_kernel" if kernel_path is KERNEL_SRC else "dot_t_"
+    kname = KERNEL_NAMES[kernel_path]
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     f_k, w_k = pick(fetch, kname), pick(write, kname)
     f_c, w_c = pick(fetch, "copyBuffer"), pick(write, "copyBuffer")
@@ -195,8 +198,11 @@ def main():
     args = ap.parse_args()
 
     if args.ingest_pmc:
-        wl_src = DOT_SRC if args.workload.startswith("dot_t") else KERNEL_SRC
-        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload, wl_src)
+        import csv
+        with open(args.ingest_pmc[0]) as f:
+            names = [r["Kernel_Name"] for r in csv.DictReader(f)]
+        counts = {src: sum(KERNEL_NAMES[src] in n for n in names) for src in KERNEL_NAMES}
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload, max(counts, key=counts.get))
         return
 
     if args.gpus != 1:
@@ -238,9 +244,9 @@ def main():
         else:
             def launch(j):
                 binding.q8_matvec_with_plan(A, Ws[j], Ss[j], plan, out=C)
-        kernel_src = KERNEL_SRC
         used_plan = plan or binding.q8_matvec_choose_plan(wl.M, wl.K, wl.N, 256, 256,
                                                            torch.cuda.get_device_properties(dev).multi_processor_count)
+        kernel_src = GEMM_SRC if used_plan.get("kind") == binding.PLAN_MATRIX else KERNEL_SRC
     elif wl.op == "q8_fused":
         A0, W0s, S0s = host0
         A = torch.from_numpy(A0).to(dev)

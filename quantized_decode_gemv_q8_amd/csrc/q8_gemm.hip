@@ -309,20 +309,24 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
     return;
   }
 
-  // Split-K: publish this split's partial [16 RT][512] with device-coherent
+  // Split-K: publish this split's partial with device-coherent (sc1) 16-byte
   // stores, count it, and let the last split of the tile sum them in K order.
+  // The partial keeps the lanes' register layout: piece ((w*8 + t)*RT + r)*64
+  // + l holds lane l's four values of tile (t, r) of wave w, so each store
+  // instruction of a wave writes 1 KB contiguously.
   constexpr int kTileElems = 16 * RT * kGemmCols;
-  float *mine = p.partial + ((size_t)tile * p.splits + split) * kTileElems;
+  constexpr int kPieces = kTileElems / 4;
+  constexpr int kCoherent = 16;  // cache policy: sc1, written through to the device's coherence point
+  const __amdgpu_buffer_rsrc_t part_rs =
+      rsrc(p.partial + (size_t)tile * p.splits * kTileElems, (uint32_t)p.splits * kTileElems * 4u);
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int m, col;
-        out_index(t, r, e, m, col);
-        __hip_atomic_store(&mine[m * kGemmCols + col], acc[t][r][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+    for (int r = 0; r < RT; ++r) {
+      const uint32_t piece = (uint32_t)(((wave * 8 + t) * RT + r) * 64 + lane);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, acc[t][r]), part_rs,
+                                             ((uint32_t)split * kPieces + piece) * 16u, 0u, kCoherent);
+    }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
@@ -332,35 +336,42 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   __syncthreads();
   if (!last_flag) return;
   // Sum the splits in K order: pairwise over groups of eight, then the groups
-  // in order (the same tree as the matvec's combine).  Each thread owns
-  // outputs tid + 256 i; they are summed eight at a time, with every load of a
-  // batch in flight together.
-  const float *src = p.partial + (size_t)tile * p.splits * kTileElems;
-  constexpr int kOut = kTileElems / kThreads;
-  constexpr int kBatch = 8;
-  for (int i0 = 0; i0 < kOut; i0 += kBatch) {
-    float total[kBatch];
+  // in order (the same tree as the matvec's combine).  Thread tid owns pieces
+  // tid + 256 i, two at a time, with every load of a batch in flight.
+  constexpr int kBatch = 2;
+  for (int i0 = 0; i0 < kPieces / kThreads; i0 += kBatch) {
+    f4 total[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) total[i] = 0.f;
+    for (int i = 0; i < kBatch; ++i) total[i] = f4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < p.splits; c += 8) {
-      float v[kBatch][8];
+      f4 v[kBatch][8];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          v[i][s] = c + s < p.splits ? __hip_atomic_load(&src[(size_t)(c + s) * kTileElems + tid + kThreads * (i0 + i)],
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                     : 0.f;
+        for (int sp = 0; sp < 8; ++sp) {
+          const uint32_t off = ((uint32_t)min(c + sp, p.splits - 1) * kPieces + tid + kThreads * (i0 + i)) * 16u;
+          const f4 x = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(part_rs, off, 0u, kCoherent));
+          v[i][sp] = c + sp < p.splits ? x : f4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
         total[i] += ((v[i][0] + v[i][1]) + (v[i][2] + v[i][3])) + ((v[i][4] + v[i][5]) + (v[i][6] + v[i][7]));
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int o = tid + kThreads * (i0 + i);
-      const int m = o / kGemmCols;
-      const int col = o - m * kGemmCols;
-      if (m < p.M && n0 + col < p.N) p.C[(size_t)m * p.N + n0 + col] = total[i];
+      // Piece -> (wave, tile, row tile, lane) -> four outputs in one column.
+      const int pc = tid + kThreads * (i0 + i);
+      const int w = pc / (8 * RT * 64);
+      const int rem = pc - w * (8 * RT * 64);
+      const int t = rem / (RT * 64);
+      const int r = (rem / 64) % RT;
+      const int l = rem % 64;
+      const int col = kWaveCols * w + 64 * (t >> 2) + 4 * (l & 15) + (t & 3);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * r + 4 * (l >> 4) + e;
+        if (m < p.M && n0 + col < p.N) p.C[(size_t)m * p.N + n0 + col] = total[i][e];
+      }
     }
   }
   if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
