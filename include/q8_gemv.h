@@ -93,7 +93,7 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
  */
 #define Q8_PLAN_STREAM 1
 #define Q8_PLAN_MATRIX 2
-#define Q8_MATRIX_MIN_ROWS 3
+#define Q8_MATRIX_MIN_ROWS 2
 #define Q8_MATRIX_MAX_ROWS 32
 typedef struct q8_plan {
   int32_t vec;

@@ -95,8 +95,11 @@ struct SFor {
 // RT: 16-row tiles of A (M <= 16 * RT).
 template <int RT>
 __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) int8_t w_lds[kBlock * kWPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t a_lds[3][16 * RT * kAPitch];
+  // Two LDS buffers: block j is staged in buffer j & 1, so staging the next
+  // block never overwrites the one other waves may still be reading, and one
+  // barrier per block suffices.
+  __shared__ __attribute__((aligned(16))) int8_t w_lds_buf[2][kBlock * kWPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t a_lds_buf[2][3][16 * RT * kAPitch];
   __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x;
@@ -196,8 +199,10 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
       const int b = b_begin + j;
       // Scales of this block for the lane's eight output columns.
       const u4 (&sv)[2] = sring[D];
-      // Block j into LDS (after every wave has finished with block j - 1).
-      lds_barrier();
+      // Block j into its LDS buffer.  The last reader of that buffer was block
+      // j - 2, which every wave finished before the barrier of block j - 1.
+      int8_t *w_lds = w_lds_buf[j & 1];
+      uint16_t(*a_lds)[16 * RT * kAPitch] = a_lds_buf[j & 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 8 * wave + 2 * i + (lane >> 5);

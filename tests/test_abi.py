@@ -54,8 +54,8 @@ def test_plan_is_valid_and_normalised(M, K, N):
     p = plan(M, K, N)
     KB = math.ceil(K / 32)
     if p["kind"] == binding.PLAN_MATRIX:
-        # matrix cores: 3..32 rows, N a multiple of 16, 512-column tiles x K splits
-        assert 3 <= M <= 32 and N % 16 == 0 and p["vec"] == 0 and p["m_tile"] == 0 and p["waves"] == 4
+        # matrix cores: 2..32 rows, N a multiple of 16, 512-column tiles x K splits
+        assert 2 <= M <= 32 and N % 16 == 0 and p["vec"] == 0 and p["m_tile"] == 0 and p["waves"] == 4
         tiles = math.ceil(N / 512)
         assert p["workgroups"] % tiles == 0
         splits = p["workgroups"] // tiles
@@ -76,19 +76,19 @@ def test_plan_vec_follows_shape_and_alignment():
     assert plan(1, 4096, 4096)["vec"] == 4      # under 2 units per CU at vec 8: 4-byte lanes
     assert plan(1, 4096, 4096, cus=64)["vec"] == 8
     assert plan(4, 4100, 5000)["vec"] == 4      # 4 rows on the stream (N % 16 != 0): vec * m_tile <= 16
-    assert plan(2, 8192, 28672)["vec"] == 8     # 2 rows * 8 <= 16
+    assert plan(2, 8192, 28680)["vec"] == 8     # 2 rows on the stream (N % 16 != 0): 2 * 8 <= 16
     assert plan(1, 64, 4100)["vec"] == 4
     assert plan(1, 64, 4096, w_align=4)["vec"] == 4
     assert plan(1, 64, 4096, s_align=8)["vec"] == 2
     assert plan(1, 64, 7)["vec"] == 1
     assert plan(8, 64, 4100)["vec"] == 2        # 8 rows on the stream (N % 16 != 0): 8 * vec <= 16
-    assert plan(2, 64, 4096)["m_tile"] == 2
+    assert plan(2, 64, 4104)["m_tile"] == 2
 
 
 def test_plan_kind_follows_rows_and_layout():
     assert plan(1, 8192, 28672)["kind"] == binding.PLAN_STREAM
-    assert plan(2, 8192, 28672)["kind"] == binding.PLAN_STREAM     # below the matrix-core row count
-    assert plan(3, 8192, 28672)["kind"] == binding.PLAN_MATRIX
+    assert plan(1, 64, 4096)["kind"] == binding.PLAN_STREAM        # one row: the matvec
+    assert plan(2, 8192, 28672)["kind"] == binding.PLAN_MATRIX
     assert plan(32, 8192, 28672)["kind"] == binding.PLAN_MATRIX
     assert plan(33, 8192, 28672)["kind"] == binding.PLAN_STREAM    # above it
     assert plan(16, 8192, 5000)["kind"] == binding.PLAN_STREAM     # N % 16 != 0
