@@ -46,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # Rotated copies per workload: enough to exceed the Infinity Cache (>= 1 GiB).
 COPIES = {"tiny": 1, "attn4096": 57, "mlp_up_8192x28672": 4, "mlp_down_28672x8192": 4,
           "ragged_m4": 47, "dot_t_16x4096x4096": 63, "mlp_gate_up_8192x28672": 2, "attn_qkv_4096": 19,
-          "batch16_8192x28672": 4}
+          "batch16_8192x28672": 4, "batch64_8192x28672": 4}
 
 
 def source_hash(paths):

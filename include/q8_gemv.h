@@ -82,10 +82,12 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
  *           of equal length (within one), at most 16/m_tile units each.  A
  *           tile shared by several workgroups is combined in K order.
  *   waves   waves per workgroup; 4 is the only value supported.
- * For Q8_PLAN_MATRIX, the matrix-core product of 2..32 rows ("dot and tensor
+ * For Q8_PLAN_MATRIX, the matrix-core product of 2..64 rows ("dot and tensor
  * cores", "Hardware paths"; A is split into three bf16 parts so that the
- * result keeps f32 accuracy): it needs N % 16 == 0 and 16-byte aligned W and
- * S, and serves q8_matvec and q8_matvec_with_plan (not the fused entry).
+ * result keeps f32 accuracy; above 32 rows it runs in 32-row passes, each
+ * reading W once): it needs N % 16 == 0 and 16-byte aligned W and S, and
+ * serves q8_matvec, q8_matvec_with_plan and a plain single-sibling fused
+ * call.
  *   vec, m_tile  must be 0.
  *   workgroups   tiles of 512 columns times K splits (a multiple of the tile
  *           count; every split gets at least one 32-row block), or 0.
@@ -94,7 +96,7 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
 #define Q8_PLAN_STREAM 1
 #define Q8_PLAN_MATRIX 2
 #define Q8_MATRIX_MIN_ROWS 2
-#define Q8_MATRIX_MAX_ROWS 32
+#define Q8_MATRIX_MAX_ROWS 64
 typedef struct q8_plan {
   int32_t vec;
   int32_t m_tile;

@@ -88,22 +88,23 @@ inline size_t gemv_lds_bytes(int vec, int m_tile, int count, int nseg) {
 // groups per tile.
 constexpr int max_segments(int count, int groups) { return (count - 1 + groups - 1) / groups + 1; }
 
-// Arguments of the Q8_0 product for 2..32 activation rows on the matrix cores:
+// Arguments of the Q8_0 product for 2..64 activation rows on the matrix cores:
 // tiles of 512 columns, each split into `splits` contiguous ranges of `bps`
-// K blocks (one workgroup each).
+// K blocks (one workgroup each); above 32 rows the launch runs 32-row passes
+// (grid z), each with its own partials and counters.
 struct GemmArgs {
   const float *A;      // [M, K]
   const int8_t *W;     // [K, N]
   const float *S;      // [KB, N]
   float *C;            // [M, N]
-  float *partial;      // [n_tiles][splits][16 * ceil(M/16)][512] split partials (splits > 1)
-  uint32_t *counters;  // [n_tiles] arrival counters, zero between calls
+  float *partial;      // [passes][n_tiles][splits][16 * RT * 512] split partials (splits > 1)
+  uint32_t *counters;  // [passes][n_tiles] arrival counters, zero between calls
   int M, K, N, KB;
   int n_tiles, splits, bps;
 };
 
 // Rows of A the matrix-core product takes at most, and its column tile.
-constexpr int kGemmMaxRows = 32;
+constexpr int kGemmMaxRows = 64;
 constexpr int kGemmTileCols = 512;
 
 hipError_t launch_gemm(const GemmArgs &args, hipStream_t stream);

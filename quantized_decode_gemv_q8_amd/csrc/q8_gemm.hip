@@ -1,4 +1,4 @@
-// Q8_0 product for a few activation rows (2 <= M <= 32) on the matrix cores:
+// Q8_0 product for a few activation rows (2 <= M <= 64) on the matrix cores:
 // C[m,n] = sum_k A[m,k] * W[k,n] * S[k/32, n], reading W and S once for all
 // rows.
 //
@@ -105,6 +105,17 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Rows beyond 16*RT run as further passes (grid z), each with its own rows
+  // of A and C, partials and counters; each pass reads W again.
+  constexpr int kTileElems = 16 * RT * kGemmCols;
+  {
+    const int pass = blockIdx.z;
+    p.A += (size_t)pass * 16 * RT * p.K;
+    p.C += (size_t)pass * 16 * RT * p.N;
+    p.M = min(16 * RT, p.M - pass * 16 * RT);
+    p.partial += (size_t)pass * p.n_tiles * p.splits * kTileElems;
+    p.counters += pass * p.n_tiles;
+  }
   const int tile = blockIdx.x;
   const int split = blockIdx.y;
   const int n0 = tile * kGemmCols;
@@ -319,7 +330,6 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   // The partial keeps the lanes' register layout: piece ((w*8 + t)*RT + r)*64
   // + l holds lane l's four values of tile (t, r) of wave w, so each store
   // instruction of a wave writes 1 KB contiguously.
-  constexpr int kTileElems = 16 * RT * kGemmCols;
   constexpr int kPieces = kTileElems / 4;
   constexpr int kCoherent = 16;  // cache policy: sc1, written through to the device's coherence point
   const __amdgpu_buffer_rsrc_t part_rs =
@@ -385,13 +395,14 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.n_tiles, (unsigned)a.splits);
+  if (a.M < 1 || a.M > kGemmMaxRows) return hipErrorInvalidValue;
   if (a.M <= 16) {
-    hipLaunchKernelGGL(q8_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, a);
-  } else if (a.M <= 32) {
-    hipLaunchKernelGGL(q8_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(q8_gemm_kernel<1>, dim3((unsigned)a.n_tiles, (unsigned)a.splits, 1), dim3(kThreads), 0,
+                       stream, a);
   } else {
-    return hipErrorInvalidValue;
+    const unsigned passes = (unsigned)((a.M + 31) / 32);
+    hipLaunchKernelGGL(q8_gemm_kernel<2>, dim3((unsigned)a.n_tiles, (unsigned)a.splits, passes), dim3(kThreads), 0,
+                       stream, a);
   }
   return hipGetLastError();
 }

@@ -1,4 +1,4 @@
-"""GPU parity of the matrix-core Q8_0 product (q8_matvec with 2..32 rows,
+"""GPU parity of the matrix-core Q8_0 product (q8_matvec with 2..64 rows,
 plan kind Q8_PLAN_MATRIX) against the CPU oracle, through the C ABI.
 
 Bar: max over outputs of |C_gpu - C_oracle| / D <= 1e-5 (D = sum of |A W S|);
@@ -39,7 +39,7 @@ def assert_parity(A, W, S, C):
     return err
 
 
-@pytest.mark.parametrize("M", [2, 5, 8, 16, 17, 24, 32])
+@pytest.mark.parametrize("M", [2, 5, 8, 16, 17, 24, 32, 33, 48, 64])
 @pytest.mark.parametrize("K,N", [(4100, 4096), (1000, 1040), (96, 512), (32, 16)])
 def test_matrix_parity(M, K, N):
     A, W, S = workloads.q8_inputs(M, K, N, (300, M, K, N))
@@ -99,6 +99,23 @@ def test_matrix_rows_are_independent():
     assert np.array_equal(C24[:8].view(np.uint32), C8.view(np.uint32))
 
 
+def test_matrix_passes_are_independent():
+    # above 32 rows the product runs in 32-row passes: each pass equals a call on its own rows
+    A, W, S = workloads.q8_inputs(61, 2000, 1024, 312)
+    C = gpu_q8(A, W, S, MATRIX)
+    for lo, hi in ((0, 32), (32, 61)):
+        part = gpu_q8(A[lo:hi], W, S, MATRIX)
+        assert np.array_equal(C[lo:hi].view(np.uint32), part.view(np.uint32))
+    assert_parity(A, W, S, C)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8])
+def test_matrix_passes_every_split(splits):
+    M, K, N = 40, 1280, 1536
+    A, W, S = workloads.q8_inputs(M, K, N, (313, splits))
+    assert_parity(A, W, S, gpu_q8(A, W, S, {"kind": binding.PLAN_MATRIX, "workgroups": 3 * splits}))
+
+
 def test_matrix_deterministic_and_zero_rows():
     A, W, S = workloads.q8_inputs(16, 4100, 4096, 306)
     A[3] = 0
@@ -127,14 +144,18 @@ def test_matrix_invalid_plans():
     A1, W1, S1 = (to_dev(x) for x in workloads.q8_inputs(1, 256, 1024, 309))
     with pytest.raises(binding.Q8Error):
         binding.q8_matvec_with_plan(A1, W1, S1, MATRIX)  # one row
+    A65, W65, S65 = (to_dev(x) for x in workloads.q8_inputs(65, 256, 1024, 314))
+    with pytest.raises(binding.Q8Error):
+        binding.q8_matvec_with_plan(A65, W65, S65, MATRIX)  # above 64 rows
     A2, W2, S2 = (to_dev(x) for x in workloads.q8_inputs(16, 256, 1000, 310))
     with pytest.raises(binding.Q8Error):
         binding.q8_matvec_with_plan(A2, W2, S2, MATRIX)  # N % 16 != 0
 
 
-def test_matrix_canaries():
-    M, K, N = 17, 1000, 1040
-    A, W, S = workloads.q8_inputs(M, K, N, 311)
+@pytest.mark.parametrize("M", [17, 45])
+def test_matrix_canaries(M):
+    K, N = 1000, 1040
+    A, W, S = workloads.q8_inputs(M, K, N, (311, M))
     pad = 4096
     buf = torch.full((M * N + 2 * pad,), float("nan"), dtype=torch.float32, device=DEV)
     buf[:pad] = 1.0
