@@ -1,4 +1,5 @@
-"""CPU oracle for the Q8_0 matvec and the i8 ``dot_t`` product.
+"""CPU oracle for the Q8_0 matvec, the i8 ``dot_t`` product and the dense f32
+``dot`` / ``dot_t`` contractions.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  The
@@ -18,9 +19,11 @@ Sources (Phobos documentation pages):
     loop is whole blocks plus one masked remainder.
   * "dot and tensor cores" (docs/language/dot-and-tensor-cores), the table of
     built-ins: dot_t(a, b) with a [M,K], b [N,K] computes a @ b^T; section
-    "Hardware paths": i8 operands accumulate in i32; section "The fused
-    epilogue": a product feeding an elementwise statement is updated as it is
-    written out (scale, and rescale-and-add).
+    "Hardware paths": i8 operands accumulate in i32, f32 operands in f32;
+    section "The k loop": dot(a, b) with a [M,K], b [K,N] is a @ b,
+    accumulated over panels of K; section "The fused epilogue": a product
+    feeding an elementwise statement is updated as it is written out (scale,
+    and rescale-and-add).
 
 Every function is pinned by tests in ``tests/test_oracle.py`` against exact
 rational arithmetic, closed forms, library special cases and hand-derived
@@ -41,4 +44,11 @@ from .q8_oracle import (  # noqa: F401
     dot_t,
     wrap_i32,
 )
-from .exact import q8_matvec_exact, q8_epilogue_exact, dot_t_loops  # noqa: F401
+from .dense import (  # noqa: F401
+    dot_f32,
+    dot_t_f32,
+    dense_normaliser,
+    dense_fused,
+    dense_fused_normaliser,
+)
+from .exact import q8_matvec_exact, q8_epilogue_exact, dot_t_loops, dense_exact  # noqa: F401

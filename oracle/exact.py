@@ -56,3 +56,16 @@ def q8_epilogue_exact(A, W, S, alpha, corr=None, C_old=None):
             r.append(y)
         out.append(r)
     return out
+
+
+def dense_exact(A, B, transposed=False):
+    """Exact sum_k A[m,k] * B[k,n] (B read as [N,K] when transposed) for f32
+    operands ("dot and tensor cores", table of built-ins), as nested Fractions
+    built one term at a time."""
+    A = np.asarray(A)
+    B = np.asarray(B)
+    M, K = A.shape
+    N = B.shape[0] if transposed else B.shape[1]
+    a = [[Fraction(float(A[m, k])) for k in range(K)] for m in range(M)]
+    b = [[Fraction(float(B[n, k] if transposed else B[k, n])) for n in range(N)] for k in range(K)]
+    return [[sum((a[m][k] * b[k][n] for k in range(K)), Fraction(0)) for n in range(N)] for m in range(M)]

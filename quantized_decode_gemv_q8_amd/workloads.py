@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the Q8_0 matvec and the i8 dot_t.
+"""Seeded synthetic inputs for the Q8_0 matvec, the i8 dot_t and the dense
+f32 dot / dot_t.
 
 This module only draws random numbers: it holds none of the method's
 arithmetic, so both the library's tests/bench and the CPU oracle can consume
@@ -8,7 +9,8 @@ Shapes and value ranges follow the decode-step projections the "Q8_0 matvec"
 page describes (one activation row against a large i8 weight matrix with one
 f32 scale per 32-row block and column).  The layer shapes stand in for
 attention / MLP projections of 7B- and 70B-class models; no trained weights
-are involved.
+are involved.  The dense f32 workloads stand in for a square f32 GEMM and for
+attention scores q @ k^T (head dimension 128), with N(0,1) operands.
 """
 
 from dataclasses import dataclass
@@ -21,7 +23,7 @@ BLOCK = 32  # Q8_0 block length along K
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str          # "q8", "q8_fused" (siblings sharing A) or "dot_t"
+    op: str          # "q8", "q8_fused" (siblings sharing A), "dot_t" (i8), "dot_f32" or "dot_t_f32"
     M: int
     K: int
     N: int
@@ -40,7 +42,13 @@ class Workload:
         if self.op in ("q8", "q8_fused"):
             per = self.K * self.N + 4 * self.KB * self.N + 4 * self.M * self.N
             return self.siblings * per + 4 * self.M * self.K
+        if self.op in ("dot_f32", "dot_t_f32"):
+            return 4 * (self.M * self.K + self.K * self.N + self.M * self.N)
         return self.M * self.K + self.N * self.K + 4 * self.M * self.N
+
+    def algorithmic_flops(self):
+        """Multiply-adds of the contraction, two flops each."""
+        return 2 * self.siblings * self.M * self.N * self.K
 
 
 WORKLOADS = {
@@ -64,6 +72,10 @@ WORKLOADS = {
     "attn_qkv_4096": Workload("attn_qkv_4096", "q8_fused", 1, 4096, 4096, "normal", "i8sym", (7, 0), siblings=3),
     # integer dot_t, weights stored one output row per row
     "dot_t_16x4096x4096": Workload("dot_t_16x4096x4096", "dot_t", 16, 4096, 4096, "i8full", "i8full", (5, 0)),
+    # dense f32 product (square GEMM) and attention scores q @ k^T * 1/sqrt(128)
+    "dot_f32_4096": Workload("dot_f32_4096", "dot_f32", 4096, 4096, 4096, "normal", "normal", (10, 0)),
+    "scores_4096x4096_d128": Workload("scores_4096x4096_d128", "dot_t_f32", 4096, 128, 4096, "normal", "normal",
+                                      (11, 0)),
 }
 
 
@@ -113,6 +125,14 @@ def dot_t_inputs(M, K, N, seed, dist="i8full"):
     return A, W
 
 
+def dense_inputs(M, K, N, seed, transposed=False, dist="normal"):
+    """(A f32 [M,K], B f32 [K,N], or [N,K] when transposed) drawn in that order."""
+    rng = rng_for(seed)
+    A = _draw(rng, dist, (M, K))
+    B = _draw(rng, dist, (N, K) if transposed else (K, N))
+    return A, B
+
+
 def make(name, copy=0):
     """Inputs of a named workload; copy j of a rotated set uses its own seed."""
     wl = WORKLOADS[name]
@@ -123,4 +143,6 @@ def make(name, copy=0):
         return q8_inputs(wl.M, wl.K, wl.N, seed, wl.a_dist, wl.w_dist)
     if wl.op == "q8_fused":
         return q8_fused_inputs(wl.M, wl.K, wl.N, wl.siblings, seed, wl.a_dist, wl.w_dist)
+    if wl.op in ("dot_f32", "dot_t_f32"):
+        return dense_inputs(wl.M, wl.K, wl.N, seed, wl.op == "dot_t_f32", wl.a_dist)
     return dot_t_inputs(wl.M, wl.K, wl.N, seed, wl.a_dist)
