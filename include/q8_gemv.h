@@ -190,6 +190,32 @@ q8_status q8_matvec_fused(const float *A, const q8_sibling *siblings, int32_t n_
 q8_status q8_dot_t(const int8_t *A, const int8_t *W, int32_t *C,
                    int64_t M, int64_t K, int64_t N, void *stream);
 
+/*
+ * Dense f32 products ("dot and tensor cores": the table of built-ins, "The k
+ * loop", "Hardware paths" and "The fused epilogue"):
+ *   q8_dot_f32    C = alpha * (A @ B)   (+ corr[m] * C),  B f32 [K, N]
+ *   q8_dot_t_f32  C = alpha * (A @ B^T) (+ corr[m] * C),  B f32 [N, K]
+ *   A  f32 [M, K] row-major, device
+ *   B  as above, row-major, device
+ *   C  f32 [M, N] row-major, device; overwritten, read only when corr != NULL;
+ *      must not alias A or B
+ *   epilogue  host pointer, or NULL for alpha = 1 and no corr (an attention
+ *      score tile is dot_t with alpha = 1/sqrt(head dim))
+ * f32 operands and f32 accumulation (full f32 products on the matrix cores,
+ * no operand rounding); each output is rounded as fmaf(corr[m], C_old,
+ * alpha * P).  Any M, K, N >= 0; every pointer 4-byte aligned; rows whose
+ * starts are all 16-byte aligned (K % 4 == 0, and N % 4 == 0 for q8_dot_f32,
+ * with 16-byte aligned A and B) take wider loads.  K == 0 gives a zero
+ * product.  Deterministic: the summation order depends only on K.
+ * Errors: Q8_ERR_INVALID (negative extent, NULL or misaligned pointer),
+ * Q8_ERR_TOO_LARGE ((M + 128) * (K + 32) or (N + 128) * (K + 32) at or above
+ * 2^30, or M * N at or above 2^31), Q8_ERR_UNSUPPORTED_DEVICE, Q8_ERR_HIP.
+ */
+q8_status q8_dot_f32(const float *A, const float *B, float *C, int64_t M, int64_t K, int64_t N,
+                     const q8_epilogue *epilogue, void *stream);
+q8_status q8_dot_t_f32(const float *A, const float *B, float *C, int64_t M, int64_t K, int64_t N,
+                       const q8_epilogue *epilogue, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *q8_status_string(q8_status s);
 

@@ -30,6 +30,8 @@ EXPORTED = (
     "q8_matvec_choose_plan",
     "q8_matvec_fused",
     "q8_dot_t",
+    "q8_dot_f32",
+    "q8_dot_t_f32",
     "q8_status_string",
     "q8_last_hip_error",
     "q8_release",
@@ -85,6 +87,10 @@ def load():
     L.q8_matvec_fused.restype = ctypes.c_int
     L.q8_dot_t.argtypes = [p, p, p, i64, i64, i64, p]
     L.q8_dot_t.restype = ctypes.c_int
+    for name in ("q8_dot_f32", "q8_dot_t_f32"):
+        fn = getattr(L, name)
+        fn.argtypes = [p, p, p, i64, i64, i64, ctypes.POINTER(Q8Epilogue), p]
+        fn.restype = ctypes.c_int
     L.q8_status_string.argtypes = [ctypes.c_int]
     L.q8_status_string.restype = ctypes.c_char_p
     L.q8_last_hip_error.argtypes = []
@@ -237,3 +243,39 @@ def q8_dot_t(A, W, out=None, stream=None):
     if st != Q8_OK:
         raise Q8Error(st, "q8_dot_t")
     return out
+
+
+def _dense(name, A, B, transposed, out, alpha, corr, stream):
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be rank 2")
+    M, K = A.shape
+    N = B.shape[0] if transposed else B.shape[1]
+    _check_tensor("A", A, torch.float32, (M, K))
+    _check_tensor("B", B, torch.float32, (N, K) if transposed else (K, N))
+    if out is None:
+        if corr is not None:
+            raise ValueError("corr reads the existing output: pass out")
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _check_tensor("out", out, torch.float32, (M, N))
+    if corr is not None:
+        _check_tensor("corr", corr, torch.float32, (M,))
+    for t in (B, out) + ((corr,) if corr is not None else ()):
+        if t.device != A.device:
+            raise ValueError("all tensors must be on one device")
+    ep = Q8Epilogue(float(alpha), corr.data_ptr() if corr is not None else None)
+    with torch.cuda.device(A.device):
+        st = getattr(load(), name)(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, K, N, ctypes.byref(ep),
+                                   _stream_handle(stream, A.device))
+    if st != Q8_OK:
+        raise Q8Error(st, name)
+    return out
+
+
+def q8_dot_f32(A, B, out=None, alpha=1.0, corr=None, stream=None):
+    """C = alpha * (A @ B) (+ corr[m] * C) for f32 A [M,K], B [K,N]; returns C (f32 [M,N])."""
+    return _dense("q8_dot_f32", A, B, False, out, alpha, corr, stream)
+
+
+def q8_dot_t_f32(A, B, out=None, alpha=1.0, corr=None, stream=None):
+    """C = alpha * (A @ B^T) (+ corr[m] * C) for f32 A [M,K], B [N,K]; returns C (f32 [M,N])."""
+    return _dense("q8_dot_t_f32", A, B, True, out, alpha, corr, stream)

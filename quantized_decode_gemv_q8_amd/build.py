@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libq8gemv.so")
 
 # The matvec instances are split by VEC so that they compile in parallel.
 SOURCES = ["q8_gemv_v16.hip", "q8_gemv_v8.hip", "q8_gemv_v4.hip", "q8_gemv_v2.hip", "q8_gemv_v1.hip",
-           "q8_gemv.hip", "q8_gemm.hip", "dot_t.hip", "q8_api.hip"]
+           "q8_gemv.hip", "q8_gemm.hip", "dense_f32.hip", "dot_t.hip", "q8_api.hip"]
 
 ARCH = "gfx950"
 # No fast-math or flush-to-zero flags.  Packed fp32 instructions are disabled

@@ -387,6 +387,40 @@ q8_status matvec_impl(const float *A, const int8_t *W, const float *S, float *C,
   return fused_impl(A, &one, 1, M, K, N, 1.0f, nullptr, req, stream);
 }
 
+// Dense f32 dot (B [K,N]) or dot_t (B [N,K]) through the epilogue.
+q8_status dense_impl(const float *A, const float *B, float *C, int64_t M, int64_t K, int64_t N, bool trans_b,
+                     const q8_epilogue *ep, void *stream_v) {
+  if (!plan_is_valid_shape(M, K, N)) return Q8_ERR_INVALID;
+  if (M == 0 || N == 0) return Q8_OK;
+  const float alpha = ep ? ep->alpha : 1.0f;
+  const float *corr = ep ? ep->corr : nullptr;
+  if ((M * K > 0 && A == nullptr) || (K * N > 0 && B == nullptr) || C == nullptr) return Q8_ERR_INVALID;
+  if (address_alignment(A) < 4 || address_alignment(B) < 4 || address_alignment(C) < 4 ||
+      address_alignment(corr) < 4)
+    return Q8_ERR_INVALID;
+  constexpr int64_t kDenseLimit = (int64_t)1 << 30;  // 32-bit byte offsets, one tile of overhang
+  if ((M + 128) * (K + 32) >= kDenseLimit || (N + 128) * (K + 32) >= kDenseLimit || M * N >= kIndexLimit)
+    return Q8_ERR_TOO_LARGE;
+  hipStream_t stream = (hipStream_t)stream_v;
+  int dev = 0;
+  DevInfo info;
+  q8_status st = current_device(&dev, &info);
+  if (st != Q8_OK) return st;
+  if (K == 0) return hip_status(q8::launch_empty_product(C, (int)M, (int)N, alpha, corr, stream));
+  const bool wide = K % 4 == 0 && (trans_b || N % 4 == 0) && address_alignment(A) >= 16 &&
+                    address_alignment(B) >= 16;
+  q8::DenseArgs a;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.corr = corr;
+  a.alpha = alpha;
+  a.M = (int)M;
+  a.K = (int)K;
+  a.N = (int)N;
+  return hip_status(q8::launch_dense_f32(a, trans_b, wide ? 4 : 1, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -441,6 +475,16 @@ q8_status q8_dot_t(const int8_t *A, const int8_t *W, int32_t *C, int64_t M, int6
   a.K = (int)K;
   a.N = (int)N;
   return hip_status(q8::launch_dot_t(a, stream));
+}
+
+q8_status q8_dot_f32(const float *A, const float *B, float *C, int64_t M, int64_t K, int64_t N,
+                     const q8_epilogue *epilogue, void *stream) {
+  return dense_impl(A, B, C, M, K, N, false, epilogue, stream);
+}
+
+q8_status q8_dot_t_f32(const float *A, const float *B, float *C, int64_t M, int64_t K, int64_t N,
+                       const q8_epilogue *epilogue, void *stream) {
+  return dense_impl(A, B, C, M, K, N, true, epilogue, stream);
 }
 
 const char *q8_status_string(q8_status s) {

@@ -109,6 +109,19 @@ constexpr int kGemmTileCols = 512;
 
 hipError_t launch_gemm(const GemmArgs &args, hipStream_t stream);
 
+// Arguments of the dense f32 dot / dot_t kernels.
+struct DenseArgs {
+  const float *A;     // [M, K]
+  const float *B;     // [K, N] (dot) or [N, K] (dot_t)
+  float *C;           // [M, N]
+  const float *corr;  // [M] epilogue row factors, or null
+  float alpha;        // epilogue scale of the product
+  int M, K, N;
+};
+
+// vec 4: every row of A and B starts 16-byte aligned; vec 1 otherwise.
+hipError_t launch_dense_f32(const DenseArgs &args, bool trans_b, int vec, hipStream_t stream);
+
 // Arguments of the i8 dot_t kernels.
 struct DotArgs {
   const int8_t *A;  // [M, K]

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH), reason="libq8gemv.
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q8_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_symbols():
