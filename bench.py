@@ -34,19 +34,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E peak
+F32_MFMA_PEAK_TFLOPS = 157.3  # MI355X published dense f32 matrix peak
 CSRC = os.path.join(ROOT, "quantized_decode_gemv_q8_amd", "csrc")
 # Sources whose hash stamps a traffic measurement (the kernel code itself).
 KERNEL_SRC = (os.path.join(CSRC, "q8_gemv_kernel.h"), os.path.join(CSRC, "q8_common.h"))
 DOT_SRC = (os.path.join(CSRC, "dot_t.hip"), os.path.join(CSRC, "q8_common.h"))
 GEMM_SRC = (os.path.join(CSRC, "q8_gemm.hip"), os.path.join(CSRC, "q8_common.h"))
+DENSE_SRC = (os.path.join(CSRC, "dense_f32.hip"), os.path.join(CSRC, "q8_common.h"))
 # Kernel-name prefix of each source set, as rocprofv3 reports it.
-KERNEL_NAMES = {KERNEL_SRC: "q8_gemv_kernel", GEMM_SRC: "q8_gemm_kernel", DOT_SRC: "dot_t_"}
+KERNEL_NAMES = {KERNEL_SRC: "q8_gemv_kernel", GEMM_SRC: "q8_gemm_kernel", DOT_SRC: "dot_t_",
+                DENSE_SRC: "dense_f32_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 # Rotated copies per workload: enough to exceed the Infinity Cache (>= 1 GiB).
 COPIES = {"tiny": 1, "attn4096": 57, "mlp_up_8192x28672": 4, "mlp_down_28672x8192": 4,
           "ragged_m4": 47, "dot_t_16x4096x4096": 63, "mlp_gate_up_8192x28672": 2, "attn_qkv_4096": 19,
-          "batch16_8192x28672": 4, "batch64_8192x28672": 4}
+          "batch16_8192x28672": 4, "batch64_8192x28672": 4, "dot_f32_4096": 1, "scores_4096x4096_d128": 1}
 
 
 def source_hash(paths):
@@ -108,28 +111,56 @@ def time_kernels(launch, steps, n_copies, torch):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
-def cpu_baseline(wl, A, W, S, budget_s=12.0):
-    """The oracle as it stands, timed on the host: whole-workload calls on copy 0,
-    repeated until about `budget_s` seconds of CPU work have been measured."""
-    import oracle
-    from threadpoolctl import threadpool_info
-
-    oracle.q8_matvec(A, W, S)  # warm-up (page-in of the f64 temporaries)
+def _time_oracle(call, budget_s):
+    call()  # warm-up (page-in of the f64 temporaries)
     times = []
     t_start = time.perf_counter()
     while len(times) < 3 or time.perf_counter() - t_start < budget_s:
         t0 = time.perf_counter()
-        oracle.q8_matvec(A, W, S)
+        call()
         times.append(time.perf_counter() - t0)
-    total = sum(times)
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return len(times), sum(times)
+
+
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+
+
+def cpu_baseline(wl, A, W, S, budget_s=12.0):
+    """The oracle as it stands, timed on the host: whole-workload calls on copy 0,
+    repeated until about `budget_s` seconds of CPU work have been measured."""
+    import oracle
+
+    n, total = _time_oracle(lambda: oracle.q8_matvec(A, W, S), budget_s)
+    threads = _blas_threads()
     return {
-        "value": round(wl.algorithmic_bytes() * len(times) / total / 1e9, 4),
+        "value": round(wl.algorithmic_bytes() * n / total / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"f64 factored oracle on the whole M={wl.M} K={wl.K} N={wl.N} workload (copy 0), "
-                  f"{len(times)} calls in {total:.1f} s; BLAS threads {threads}, numpy upcasts single-threaded",
+                  f"{n} calls in {total:.1f} s; BLAS threads {threads}, numpy upcasts single-threaded",
+    }
+
+
+def cpu_baseline_dense(wl, A, B, alpha, rows=512, budget_s=12.0):
+    """The dense oracle on a bounded sample: the first `rows` rows of A against
+    all of B (copy 0), in TFLOP/s of the workload's arithmetic."""
+    import oracle
+
+    tr = wl.op == "dot_t_f32"
+    As = np.ascontiguousarray(A[:rows])
+    n, total = _time_oracle(lambda: oracle.dense_fused(As, B, tr, alpha), budget_s)
+    threads = _blas_threads()
+    flops = 2.0 * As.shape[0] * wl.N * wl.K
+    return {
+        "value": round(flops * n / total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"f64 dense oracle on rows 0..{As.shape[0] - 1} of A against all of B (K={wl.K} N={wl.N}, "
+                  f"copy 0), {n} calls in {total:.1f} s; BLAS threads {threads}",
     }
 
 
@@ -266,6 +297,22 @@ def main():
                 binding.q8_matvec(A, Ws[j][g], Ss[j][g], out=Cs[g])
         kernel_src = KERNEL_SRC
         used_plan = plan
+    elif wl.op in ("dot_f32", "dot_t_f32"):
+        A0, B0 = host0
+        tr = wl.op == "dot_t_f32"
+        alpha = float(1.0 / np.sqrt(wl.K)) if tr else 1.0  # attention scores take 1/sqrt(head dim)
+        As, Bs = [], []
+        for j in range(n_copies):
+            Aj, Bj = host0 if j == 0 else workloads.make(wl.name, j)
+            As.append(torch.from_numpy(Aj).to(dev))
+            Bs.append(torch.from_numpy(Bj).to(dev))
+        C = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+        fn = binding.q8_dot_t_f32 if tr else binding.q8_dot_f32
+
+        def launch(j):
+            fn(As[j], Bs[j], out=C, alpha=alpha)
+        kernel_src = DENSE_SRC
+        used_plan = None
     else:
         A0, W0 = host0
         A = torch.from_numpy(A0).to(dev)
@@ -284,7 +331,15 @@ def main():
         torch.cuda.synchronize()
         cols = np.unique(np.random.default_rng(0).integers(0, wl.N, 512))
         Cg = C.cpu().numpy()[:, cols]
-        if wl.op in ("q8", "q8_fused"):
+        if wl.op in ("dot_f32", "dot_t_f32"):
+            rows = np.unique(np.random.default_rng(0).integers(0, wl.M, 64))
+            Ar = np.ascontiguousarray(A0[rows])
+            err = oracle.normalised_error(C.cpu().numpy()[rows], oracle.dense_fused(Ar, B0, tr, alpha),
+                                          oracle.dense_fused_normaliser(Ar, B0, tr, alpha))
+            if not err <= 1e-5:
+                raise SystemExit(f"parity check failed: normalised error {err:.3e}")
+            cols = rows  # reported below as the sample size
+        elif wl.op in ("q8", "q8_fused"):
             pairs = [(W0, S0, Cg)] if wl.op == "q8" else \
                 [(W0s[g], S0s[g], Cs[g].cpu().numpy()[:, cols]) for g in range(wl.siblings)]
             for Wg, Sg, Cgg in pairs:
@@ -295,7 +350,8 @@ def main():
         else:
             if not np.array_equal(Cg, oracle.dot_t(A0, np.ascontiguousarray(W0[cols]))):
                 raise SystemExit("parity check failed: dot_t differs from the oracle")
-        print(f"[bench] parity ok on {len(cols)} sampled columns", file=sys.stderr, flush=True)
+        what = "rows" if wl.op in ("dot_f32", "dot_t_f32") else "columns"
+        print(f"[bench] parity ok on {len(cols)} sampled {what}", file=sys.stderr, flush=True)
 
     if args.pmc_pass:
         for i in range(args.warmup + args.steps):
@@ -330,11 +386,18 @@ def main():
               file=sys.stderr, flush=True)
 
     traffic = measured_traffic(wl.name, kernel_src)
+    dense = wl.op in ("dot_f32", "dot_t_f32")
+    if dense:
+        # The dense products are bound by the f32 matrix rate: value and roofline in TFLOP/s.
+        flops = wl.algorithmic_flops()
+        value = flops * args.steps / wall / 1e12
+        achieved = flops / launch_s / 1e12
     headline = "Q8_0 GEMV effective HBM GB/s and % of peak at K=8192,N=28672, M=1"
     result = {
-        "metric": headline if wl.name == "mlp_up_8192x28672" else f"effective HBM GB/s, {wl.name}",
+        "metric": headline if wl.name == "mlp_up_8192x28672" else
+        (f"f32 TFLOP/s, {wl.name}" if dense else f"effective HBM GB/s, {wl.name}"),
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": "TFLOP/s" if dense else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -346,10 +409,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "siblings": wl.siblings,
                    "rotated_copies": n_copies,
-                   "algorithmic_bytes_per_step": nbytes, "plan": used_plan},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+                   "algorithmic_bytes_per_step": nbytes, "plan": used_plan,
+                   **({"algorithmic_flops_per_step": wl.algorithmic_flops()} if dense else {})},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F32_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / F32_MFMA_PEAK_TFLOPS, 4), "traffic": traffic}
+        if dense else
+        {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "pct_of_peak": round(100.0 * value / (F32_MFMA_PEAK_TFLOPS if dense else HBM_PEAK_GBS), 2),
         "launch_us": round(launch_s * 1e6, 3),
         "per_launch_us": {"mean": round(float(np.mean(per)) * 1e3, 3), "median": round(float(np.median(per)) * 1e3, 3),
                       "p10": round(float(np.percentile(per, 10)) * 1e3, 3),
@@ -360,6 +427,9 @@ def main():
     if not args.no_cpu_baseline and wl.op == "q8":
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, A0, W0, S0)
+    elif not args.no_cpu_baseline and dense:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_dense(wl, A0, B0, alpha)
     print(json.dumps(result), flush=True)
 
 
