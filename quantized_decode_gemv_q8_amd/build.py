@@ -33,6 +33,12 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source additions.  The matrix-core product keeps its MFMA results in
+# ordinary VGPRs (the scale FMAs read every result; with accumulation
+# registers each read would need an extra copy instruction).
+EXTRA_FLAGS = {"q8_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc():
     cand = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     return cand
@@ -40,7 +46,8 @@ def _hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -168,10 +168,9 @@ bool plan_is_valid_shape(int64_t M, int64_t K, int64_t N) {
 }
 
 // Fills in a matrix-core plan: 512-column tiles times K splits.  Automatic
-// splits aim at two workgroups per CU for up to 16 rows (that instance's
-// registers leave room for two; its workgroups are bound by instruction
-// issue, so a second one per CU hides the first one's waits: 73.8 -> 66.6 us
-// at M=16, K=8192, N=28672) and one for up to 32 rows, at most 8 splits
+// splits aim at two workgroups per CU for up to 16 rows (that instance keeps
+// to 128 registers so that two 8-wave workgroups fit a CU, and a second one
+// per CU hides the first one's waits) and one for more rows, at most 8 splits
 // (each split's partial is a whole 16*ceil(M/16) x 512 tile, read back by the
 // combine), and at most 64 blocks per split (the sequential sum over a
 // split's blocks stays short).
@@ -194,7 +193,7 @@ bool finish_gemm_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan 
   const int64_t rows = M <= 16 ? 16 : 32 * ceil_div(M, 32);  // partial rows over all passes
   if (n_tiles * splits * rows * q8::kGemmTileCols >= kIndexLimit) return false;
   pl->workgroups = (int32_t)(n_tiles * splits);
-  pl->waves = q8::kWaves;
+  pl->waves = q8::kGemmWaves;
   return true;
 }
 
@@ -203,7 +202,6 @@ bool finish_gemm_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan 
 q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w_align, int64_t s_align,
                        int32_t num_cus, bool matrix_ok, const q8_plan *req, q8_plan *out) {
   q8_plan pl = req ? *req : q8_plan{0, 0, 0, 0, 0};
-  if (pl.waves != 0 && pl.waves != q8::kWaves) return Q8_ERR_INVALID;
   if (pl.kind != 0 && pl.kind != Q8_PLAN_STREAM && pl.kind != Q8_PLAN_MATRIX) return Q8_ERR_INVALID;
   const bool matrix_fits = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 && N % 16 == 0 &&
                            w_align % 16 == 0 && s_align % 16 == 0;
@@ -212,11 +210,13 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
                   ? Q8_PLAN_MATRIX
                   : Q8_PLAN_STREAM;
   if (pl.kind == Q8_PLAN_MATRIX) {
+    if (pl.waves != 0 && pl.waves != q8::kGemmWaves) return Q8_ERR_INVALID;
     if (!matrix_fits || pl.vec != 0 || pl.m_tile != 0 || pl.workgroups < 0) return Q8_ERR_INVALID;
     if (!finish_gemm_plan(M, K, N, num_cus, &pl)) return Q8_ERR_INVALID;
     *out = pl;
     return Q8_OK;
   }
+  if (pl.waves != 0 && pl.waves != q8::kWaves) return Q8_ERR_INVALID;
   if (pl.m_tile == 0) pl.m_tile = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
   if (pl.m_tile != 1 && pl.m_tile != 2 && pl.m_tile != 4 && pl.m_tile != 8) return Q8_ERR_INVALID;
   if (pl.vec == 0) {

@@ -103,9 +103,11 @@ struct GemmArgs {
   int n_tiles, splits, bps;
 };
 
-// Rows of A the matrix-core product takes at most, and its column tile.
+// Rows of A the matrix-core product takes at most, its column tile and its
+// waves per workgroup.
 constexpr int kGemmMaxRows = 64;
 constexpr int kGemmTileCols = 512;
+constexpr int kGemmWaves = 8;
 
 hipError_t launch_gemm(const GemmArgs &args, hipStream_t stream);
 

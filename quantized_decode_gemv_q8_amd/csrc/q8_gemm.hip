@@ -20,21 +20,24 @@
 // block takes three MFMAs, one per part, into the same f32 accumulator.
 //
 // Work decomposition:
-//   * A workgroup (four wave64s) owns a tile of 512 columns and a contiguous
-//     range of K blocks (a split); the splits of a tile are combined as in the
-//     matvec: device-coherent partials, an arrival counter, and the last
-//     arrival sums the splits in K order.
+//   * A workgroup (eight wave64s) owns a tile of 512 columns and a
+//     contiguous range of K blocks (a split); the splits of a tile are
+//     combined as in the matvec: device-coherent partials, an arrival
+//     counter, and the last arrival sums the splits in K order.
 //   * Per block the workgroup loads W[32 rows, 512 columns] with 16-byte
 //     loads (a wave instruction reads two whole 512-byte row segments) into
-//     LDS, several blocks ahead in registers.  A's block (M x 32) is split
-//     into its three bf16 parts in LDS once per workgroup.
-//   * Wave w computes columns [128w, 128w + 128) as eight 16x16 output tiles
-//     per 16 rows of A.  For the B operand a lane needs eight consecutive k of
-//     one column; it reads four columns x eight rows as dwords from LDS and
+//     LDS, two blocks ahead in registers.  A's block (M x 32) is split into
+//     its three bf16 parts in LDS once per workgroup.
+//   * Wave w computes columns [64w, 64w + 64) as four 16x16 output tiles per
+//     16 rows of A.  For the B operand a lane needs eight consecutive k of one
+//     column; it reads four columns x eight rows as dwords from LDS and
 //     converts the bytes straight into bf16 pairs in k order (a byte-selecting
 //     convert and a byte permute), so the transpose costs nothing extra.
-//     Lane l of tile i of column group q supplies column 64q + 4(l%16) + i,
-//     which is the column its outputs belong to.
+//     Lane l of tile i supplies column 4(l%16) + i of the wave's 64, which is
+//     the column its outputs belong to.
+//   * Eight waves of at most 128 registers (up to 16 rows) let two
+//     workgroups share a CU with four waves per SIMD, so one wave's convert
+//     or wait overlaps another's matrix ops.
 #include <type_traits>
 
 #include "q8_common.h"
@@ -47,10 +50,15 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmCols = kGemmTileCols;   // columns per workgroup tile
-constexpr int kWaveCols = 128;             // columns per wave
+constexpr int kGW = kGemmWaves;            // waves per workgroup
+constexpr int kGThreads = 64 * kGW;
+constexpr int kWaveCols = kGemmCols / kGW; // columns per wave (64)
+constexpr int kWaveTiles = kWaveCols / 16; // 16-column output tiles per wave
+constexpr int kWaveGroups = kWaveCols / 64;  // groups of 64 columns per wave
+constexpr int kRowPairs = kBlock / (2 * kGW);  // W row pairs per wave and block
 constexpr int kWPitch = kGemmCols + 16;    // LDS row pitch of a W block, bytes (16-byte aligned rows)
 constexpr int kAPitch = 40;                // LDS row pitch of an A block part, bf16 (80 bytes)
-constexpr int kDepthG = 3;                 // W blocks held in registers ahead of the one in LDS
+constexpr int kDepthG = 2;                 // W blocks held in registers ahead of the one in LDS
 constexpr int kStreamPolicyG = 2;          // non-temporal: W and S are read once
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
@@ -94,7 +102,7 @@ struct SFor {
 
 // RT: 16-row tiles of A (M <= 16 * RT).
 template <int RT>
-__global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 : 2))) void q8_gemm_kernel(GemmArgs p) {
   // Two LDS buffers: block j is staged in buffer j & 1, so staging the next
   // block never overwrites the one other waves may still be reading, and one
   // barrier per block suffices.
@@ -131,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   const uint32_t s_bytes = (uint32_t)p.KB * (uint32_t)p.N * 4u;
   const uint32_t a_bytes = (uint32_t)p.M * (uint32_t)p.K * 4u;
 
-  // This thread's 16-byte piece of a W block: row 8*wave + 2*i + lane/32,
-  // columns n0 + 16*(lane%32) .. +15, for i = 0..3.  The row pair's first
+  // This thread's 16-byte piece of a W block: row (32/kGW)*wave + 2*i +
+  // lane/32, columns n0 + 16*(lane%32) .. +15, for i < kRowPairs.  The row pair's first
   // row goes into the wave-uniform scalar offset, clamped to K - 1; the
   // second is a per-lane step of one row, taken only while that row exists.
   // Columns past N (the ragged last tile; N is a multiple of 16) read column
@@ -140,11 +148,11 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   const int wcol = n0 + 16 * (lane & 31);
   const uint32_t w_voff = wcol < p.N ? (uint32_t)wcol : 0u;
   const bool upper = (lane >> 5) != 0;
-  auto load_w = [&](int b, bool live, u4 (&x)[4]) {
+  auto load_w = [&](int b, bool live, u4 (&x)[kRowPairs]) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(p.W, live ? w_bytes : 0u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = min(b * kBlock + 8 * wave + 2 * i, p.K - 1);
+    for (int i = 0; i < kRowPairs; ++i) {
+      const int r = min(b * kBlock + (kBlock / kGW) * wave + 2 * i, p.K - 1);
       const uint32_t voff = w_voff + (upper && r + 1 < p.K ? (uint32_t)p.N : 0u);
       x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (uint32_t)r * (uint32_t)p.N, kStreamPolicyG);
     }
@@ -154,48 +162,48 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   // 64q + 4(l%16) .. +3 of the wave's 128.
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
-  uint32_t s_voff[2];
+  uint32_t s_voff[kWaveGroups];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kWaveGroups; ++q) {
     const int c = n0 + kWaveCols * wave + 64 * q + 4 * c16;
     s_voff[q] = c < p.N ? (uint32_t)c * 4u : 0u;
   }
 
   // Activation block b: elements e = tid + 256 j of the 16*RT x 32 block.
-  constexpr int kAElems = 16 * RT * kBlock / kThreads;  // per thread
+  constexpr int kAElems = 16 * RT * kBlock / kGThreads;  // per thread
   // Elements past M or K load element 0; they are replaced by zero when the
   // block is staged (not here, which would wait for the load at once).
   auto a_ok = [&](int b, int j) {
-    const int e = tid + kThreads * j;
+    const int e = tid + kGThreads * j;
     return (e >> 5) < p.M && b * kBlock + (e & 31) < p.K;
   };
   auto load_a = [&](int b, bool live, float (&v)[kAElems]) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(p.A, live ? a_bytes : 0u);
 #pragma unroll
     for (int j = 0; j < kAElems; ++j) {
-      const int e = tid + kThreads * j;
+      const int e = tid + kGThreads * j;
       const uint32_t off = a_ok(b, j) ? ((uint32_t)(e >> 5) * (uint32_t)p.K + (uint32_t)(b * kBlock + (e & 31))) * 4u : 0u;
       v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0u, 0));
     }
   };
 
-  f4 acc[8][RT];
+  f4 acc[kWaveTiles][RT];
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < kWaveTiles; ++t)
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[t][r] = f4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_s = [&](int b, bool live, u4 (&sv)[2]) {
+  auto load_s = [&](int b, bool live, u4 (&sv)[kWaveGroups]) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(p.S, live ? s_bytes : 0u);
     const uint32_t soff = (uint32_t)min(b, p.KB - 1) * (uint32_t)p.N * 4u;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) sv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, s_voff[q], soff, kStreamPolicyG);
+    for (int q = 0; q < kWaveGroups; ++q) sv[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, s_voff[q], soff, kStreamPolicyG);
   };
 
   // Register ring: W, A and S of blocks b_begin + j for j < kDepthG are in flight.
-  u4 wring[kDepthG][4];
+  u4 wring[kDepthG][kRowPairs];
   float aring[kDepthG][kAElems];
-  u4 sring[kDepthG][2];
+  u4 sring[kDepthG][kWaveGroups];
 #pragma unroll
   for (int d = 0; d < kDepthG; ++d) {
     load_w(b_begin + d, d < nb, wring[d]);
@@ -209,19 +217,19 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
     constexpr bool REFILL = decltype(refill_)::value;
       const int b = b_begin + j;
       // Scales of this block for the lane's eight output columns.
-      const u4 (&sv)[2] = sring[D];
+      const u4 (&sv)[kWaveGroups] = sring[D];
       // Block j into its LDS buffer.  The last reader of that buffer was block
       // j - 2, which every wave finished before the barrier of block j - 1.
       int8_t *w_lds = w_lds_buf[j & 1];
       uint16_t(*a_lds)[16 * RT * kAPitch] = a_lds_buf[j & 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 8 * wave + 2 * i + (lane >> 5);
+      for (int i = 0; i < kRowPairs; ++i) {
+        const int row = (kBlock / kGW) * wave + 2 * i + (lane >> 5);
         *reinterpret_cast<u4 *>(&w_lds[row * kWPitch + 16 * (lane & 31)]) = wring[D][i];
       }
 #pragma unroll
       for (int jj = 0; jj < kAElems; ++jj) {
-        const int e = tid + kThreads * jj;
+        const int e = tid + kGThreads * jj;
         const int m = e >> 5;
         const int k = e & 31;
         const float a = a_ok(b, jj) ? aring[D][jj] : 0.f;
@@ -249,9 +257,9 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
           aop[part][r] = *reinterpret_cast<const bf16x8 *>(&a_lds[part][(16 * r + c16) * kAPitch + 8 * g4]);
       // B operands of the wave's eight column tiles: four columns x eight
       // rows of W per lane and column group, as bf16 pairs in k order.
-      bf16x8 bop[8];
+      bf16x8 bop[kWaveTiles];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kWaveGroups; ++q) {
         uint32_t x[8];
         const int cb = kWaveCols * wave + 64 * q + 4 * c16;
 #pragma unroll
@@ -268,21 +276,21 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
       }
       // The block's unscaled partial of every tile: one MFMA per part of A,
       // part-major so that consecutive MFMAs are independent.
-      f4 part[8][RT];
+      f4 part[kWaveTiles][RT];
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < kWaveTiles; ++t)
 #pragma unroll
         for (int r = 0; r < RT; ++r) part[t][r] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int pa = 0; pa < 3; ++pa)
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int t = 0; t < kWaveTiles; ++t)
 #pragma unroll
           for (int r = 0; r < RT; ++r)
             part[t][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[pa][r], bop[t], part[t][r], 0, 0, 0);
       // "Factoring out the scale": one multiply per block and column.
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < kWaveTiles; ++t) {
         const float s = reinterpret_cast<const float *>(&sv[t >> 2])[t & 3];
 #pragma unroll
         for (int r = 0; r < RT; ++r)
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   };
   if (p.splits == 1) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < kWaveTiles; ++t)
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -335,10 +343,10 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t part_rs =
       rsrc(p.partial + (size_t)tile * p.splits * kTileElems, (uint32_t)p.splits * kTileElems * 4u);
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < kWaveTiles; ++t)
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const uint32_t piece = (uint32_t)(((wave * 8 + t) * RT + r) * 64 + lane);
+      const uint32_t piece = (uint32_t)(((wave * kWaveTiles + t) * RT + r) * 64 + lane);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, acc[t][r]), part_rs,
                                              ((uint32_t)split * kPieces + piece) * 16u, 0u, kCoherent);
     }
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
   // in order (the same tree as the matvec's combine).  Thread tid owns pieces
   // tid + 256 i, two at a time, with every load of a batch in flight.
   constexpr int kBatch = 2;
-  for (int i0 = 0; i0 < kPieces / kThreads; i0 += kBatch) {
+  for (int i0 = 0; i0 < kPieces / kGThreads; i0 += kBatch) {
     f4 total[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) total[i] = f4{0.f, 0.f, 0.f, 0.f};
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
       for (int i = 0; i < kBatch; ++i)
 #pragma unroll
         for (int sp = 0; sp < 8; ++sp) {
-          const uint32_t off = ((uint32_t)min(c + sp, p.splits - 1) * kPieces + tid + kThreads * (i0 + i)) * 16u;
+          const uint32_t off = ((uint32_t)min(c + sp, p.splits - 1) * kPieces + tid + kGThreads * (i0 + i)) * 16u;
           const f4 x = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(part_rs, off, 0u, kCoherent));
           v[i][sp] = c + sp < p.splits ? x : f4{0.f, 0.f, 0.f, 0.f};
         }
@@ -375,9 +383,9 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       // Piece -> (wave, tile, row tile, lane) -> four outputs in one column.
-      const int pc = tid + kThreads * (i0 + i);
-      const int w = pc / (8 * RT * 64);
-      const int rem = pc - w * (8 * RT * 64);
+      const int pc = tid + kGThreads * (i0 + i);
+      const int w = pc / (kWaveTiles * RT * 64);
+      const int rem = pc - w * (kWaveTiles * RT * 64);
       const int t = rem / (RT * 64);
       const int r = (rem / 64) % RT;
       const int l = rem % 64;
@@ -397,11 +405,11 @@ __global__ __launch_bounds__(kThreads) void q8_gemm_kernel(GemmArgs p) {
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
   if (a.M < 1 || a.M > kGemmMaxRows) return hipErrorInvalidValue;
   if (a.M <= 16) {
-    hipLaunchKernelGGL(q8_gemm_kernel<1>, dim3((unsigned)a.n_tiles, (unsigned)a.splits, 1), dim3(kThreads), 0,
+    hipLaunchKernelGGL(q8_gemm_kernel<1>, dim3((unsigned)a.n_tiles, (unsigned)a.splits, 1), dim3(kGThreads), 0,
                        stream, a);
   } else {
     const unsigned passes = (unsigned)((a.M + 31) / 32);
-    hipLaunchKernelGGL(q8_gemm_kernel<2>, dim3((unsigned)a.n_tiles, (unsigned)a.splits, passes), dim3(kThreads), 0,
+    hipLaunchKernelGGL(q8_gemm_kernel<2>, dim3((unsigned)a.n_tiles, (unsigned)a.splits, passes), dim3(kGThreads), 0,
                        stream, a);
   }
   return hipGetLastError();

@@ -54,8 +54,8 @@ def test_plan_is_valid_and_normalised(M, K, N):
     p = plan(M, K, N)
     KB = math.ceil(K / 32)
     if p["kind"] == binding.PLAN_MATRIX:
-        # matrix cores: 2..32 rows, N a multiple of 16, 512-column tiles x K splits
-        assert 2 <= M <= 32 and N % 16 == 0 and p["vec"] == 0 and p["m_tile"] == 0 and p["waves"] == 4
+        # matrix cores: 2..64 rows, N a multiple of 16, 512-column tiles x K splits, 8 waves
+        assert 2 <= M <= 64 and N % 16 == 0 and p["vec"] == 0 and p["m_tile"] == 0 and p["waves"] == 8
         tiles = math.ceil(N / 512)
         assert p["workgroups"] % tiles == 0
         splits = p["workgroups"] // tiles

@@ -138,7 +138,7 @@ def test_matrix_power_of_two_scaling_is_exact():
 def test_matrix_invalid_plans():
     A, W, S = (to_dev(x) for x in workloads.q8_inputs(16, 256, 1024, 308))
     for bad in ({"kind": 2, "vec": 8}, {"kind": 2, "m_tile": 4}, {"kind": 2, "workgroups": 3},
-                {"kind": 3}, {"kind": 2, "workgroups": 2 * 9}):
+                {"kind": 3}, {"kind": 2, "workgroups": 2 * 9}, {"kind": 2, "waves": 4}):
         with pytest.raises(binding.Q8Error):
             binding.q8_matvec_with_plan(A, W, S, bad)
     A1, W1, S1 = (to_dev(x) for x in workloads.q8_inputs(1, 256, 1024, 309))
