@@ -190,7 +190,7 @@ bool finish_gemm_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan 
     splits = pl->workgroups / n_tiles;
     if (splits < 1 || splits > KB || ceil_div(KB, ceil_div(KB, splits)) != splits) return false;
   }
-  const int64_t rows = M <= 16 ? 16 : 32 * ceil_div(M, 32);  // partial rows over all passes
+  const int64_t rows = 16 * q8::gemm_row_tiles(M) * ceil_div(M, 16 * q8::gemm_row_tiles(M));  // over all passes
   if (n_tiles * splits * rows * q8::kGemmTileCols >= kIndexLimit) return false;
   pl->workgroups = (int32_t)(n_tiles * splits);
   pl->waves = q8::kGemmWaves;
@@ -334,8 +334,8 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
     g.splits = pl.workgroups / g.n_tiles;
     g.bps = (int)ceil_div(KB, g.splits);
     Workspace ws;
-    // Partials and counters per 32-row pass (16 rows when M <= 16).
-    const int64_t rows = M <= 16 ? 16 : 32;
+    // Partials and counters per pass of 16 * gemm_row_tiles(M) rows.
+    const int64_t rows = 16 * q8::gemm_row_tiles(M);
     const int64_t passes = ceil_div(M, rows);
     const size_t part =
         g.splits > 1 ? (size_t)(passes * g.n_tiles * g.splits * rows * q8::kGemmTileCols) : 1;

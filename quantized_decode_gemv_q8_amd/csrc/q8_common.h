@@ -90,8 +90,8 @@ constexpr int max_segments(int count, int groups) { return (count - 1 + groups -
 
 // Arguments of the Q8_0 product for 2..64 activation rows on the matrix cores:
 // tiles of 512 columns, each split into `splits` contiguous ranges of `bps`
-// K blocks (one workgroup each); above 32 rows the launch runs 32-row passes
-// (grid z), each with its own partials and counters.
+// K blocks (one workgroup each).  Rows beyond one instance's 16 * RT would run
+// as passes on grid z, each with its own partials and counters.
 struct GemmArgs {
   const float *A;      // [M, K]
   const int8_t *W;     // [K, N]
@@ -108,6 +108,9 @@ struct GemmArgs {
 constexpr int kGemmMaxRows = 64;
 constexpr int kGemmTileCols = 512;
 constexpr int kGemmWaves = 8;
+// 16-row tiles of A per pass of the matrix-core product: 1 up to 16 rows, 2 up
+// to 32, 4 up to 64 (one pass reads W once for all of them).
+constexpr int gemm_row_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 
 hipError_t launch_gemm(const GemmArgs &args, hipStream_t stream);
 

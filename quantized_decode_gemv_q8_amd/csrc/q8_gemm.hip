@@ -113,8 +113,9 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Rows beyond 16*RT run as further passes (grid z), each with its own rows
-  // of A and C, partials and counters; each pass reads W again.
+  // Rows beyond 16*RT would run as further passes (grid z), each with its own
+  // rows of A and C, partials and counters, reading W again; with RT chosen
+  // by gemm_row_tiles every launch up to kGemmMaxRows rows is one pass.
   constexpr int kTileElems = 16 * RT * kGemmCols;
   {
     const int pass = blockIdx.z;
@@ -404,13 +405,14 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
   if (a.M < 1 || a.M > kGemmMaxRows) return hipErrorInvalidValue;
-  if (a.M <= 16) {
-    hipLaunchKernelGGL(q8_gemm_kernel<1>, dim3((unsigned)a.n_tiles, (unsigned)a.splits, 1), dim3(kGThreads), 0,
-                       stream, a);
+  const int rt = gemm_row_tiles(a.M);
+  const dim3 grid((unsigned)a.n_tiles, (unsigned)a.splits, (unsigned)((a.M + 16 * rt - 1) / (16 * rt)));
+  if (rt == 1) {
+    hipLaunchKernelGGL(q8_gemm_kernel<1>, grid, dim3(kGThreads), 0, stream, a);
+  } else if (rt == 2) {
+    hipLaunchKernelGGL(q8_gemm_kernel<2>, grid, dim3(kGThreads), 0, stream, a);
   } else {
-    const unsigned passes = (unsigned)((a.M + 31) / 32);
-    hipLaunchKernelGGL(q8_gemm_kernel<2>, dim3((unsigned)a.n_tiles, (unsigned)a.splits, passes), dim3(kGThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL(q8_gemm_kernel<4>, grid, dim3(kGThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

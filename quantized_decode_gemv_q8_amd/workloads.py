@@ -61,7 +61,7 @@ WORKLOADS = {
     "mlp_down_28672x8192": Workload("mlp_down_28672x8192", "q8", 1, 28672, 8192, "normal", "i8sym", (3, 1)),
     # a batch of 16 decode rows against the up-projection (matrix-core product)
     "batch16_8192x28672": Workload("batch16_8192x28672", "q8", 16, 8192, 28672, "normal", "i8sym", (8, 0)),
-    # 64 rows: two 32-row passes of the matrix-core product
+    # 64 rows: the matrix-core product's 64-row instance
     "batch64_8192x28672": Workload("batch64_8192x28672", "q8", 64, 8192, 28672, "normal", "i8sym", (9, 0)),
     # ragged batched case: 4 rows, K=4100 (last block 4 rows), N=5000
     "ragged_m4": Workload("ragged_m4", "q8", 4, 4100, 5000, "normal", "i8sym", (4, 0)),

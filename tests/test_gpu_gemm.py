@@ -99,8 +99,8 @@ def test_matrix_rows_are_independent():
     assert np.array_equal(C24[:8].view(np.uint32), C8.view(np.uint32))
 
 
-def test_matrix_passes_are_independent():
-    # above 32 rows the product runs in 32-row passes: each pass equals a call on its own rows
+def test_matrix_row_blocks_are_independent():
+    # the 64-row instance's rows equal calls on 32 rows (and on the 29 left over)
     A, W, S = workloads.q8_inputs(61, 2000, 1024, 312)
     C = gpu_q8(A, W, S, MATRIX)
     for lo, hi in ((0, 32), (32, 61)):
@@ -110,7 +110,7 @@ def test_matrix_passes_are_independent():
 
 
 @pytest.mark.parametrize("splits", [1, 3, 8])
-def test_matrix_passes_every_split(splits):
+def test_matrix_64_row_instance_every_split(splits):
     M, K, N = 40, 1280, 1536
     A, W, S = workloads.q8_inputs(M, K, N, (313, splits))
     assert_parity(A, W, S, gpu_q8(A, W, S, {"kind": binding.PLAN_MATRIX, "workgroups": 3 * splits}))
