@@ -260,12 +260,27 @@ __global__ __launch_bounds__(kThreads) void dense_f32_kernel(DenseArgs p) {
   }
 
   // Epilogue.  Accumulator register r of lane (r32, half) in tile (i, j) is
-  // row 8 (r / 4) + 4 half + r % 4 and column r32 of that 32 x 32 tile.
+  // row 8 (r / 4) + 4 half + r % 4 and column r32 of that 32 x 32 tile.  A
+  // tile wholly inside C and an epilogue without row factors (both uniform
+  // over the workgroup) take straight-line stores.
+  const bool whole = m0 + kTM <= p.M && n0 + kTN <= p.N;
+  const int m_w = m0 + 64 * wm + 4 * half, n_w = n0 + 64 * wn + r32;
+  if (whole && p.corr == nullptr) {
+    float *base = p.C + (size_t)m_w * p.N + n_w;
+    SFor<0, 2>::run([&](auto i) {
+      SFor<0, 2>::run([&](auto j) {
+        SFor<0, 16>::run([&](auto r) {
+          base[(size_t)(32 * i + 8 * (r / 4) + r % 4) * p.N + 32 * j] = p.alpha * acc[i][j][(int)r];
+        });
+      });
+    });
+    return;
+  }
   SFor<0, 2>::run([&](auto i) {
     SFor<0, 2>::run([&](auto j) {
-      const int n = n0 + 64 * wn + 32 * j + r32;
+      const int n = n_w + 32 * j;
       SFor<0, 16>::run([&](auto r) {
-        const int m = m0 + 64 * wm + 32 * i + 8 * (r / 4) + 4 * half + r % 4;
+        const int m = m_w + 32 * i + 8 * (r / 4) + r % 4;
         if (m < p.M && n < p.N) {
           float *c = p.C + (size_t)m * p.N + n;
           float y = p.alpha * acc[i][j][(int)r];

@@ -155,5 +155,27 @@ def test_dot_t_rejects_bad_extents_and_pointers():
     assert L.q8_dot_t(null, null, null, 0, 4, 4, null) == binding.Q8_OK
 
 
+def test_dense_rejects_bad_extents_and_pointers():
+    L = binding.load()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1002)  # 2-byte aligned: not an f32 array
+    ep = binding.Q8Epilogue(1.0, None)
+    for fn in (L.q8_dot_f32, L.q8_dot_t_f32):
+        assert fn(fake, fake, fake, -1, 4, 4, ctypes.byref(ep), None) == binding.Q8_ERR_INVALID
+        assert fn(fake, fake, fake, 4, -1, 4, None, None) == binding.Q8_ERR_INVALID
+        assert fn(None, fake, fake, 4, 4, 4, None, None) == binding.Q8_ERR_INVALID
+        assert fn(fake, None, fake, 4, 4, 4, None, None) == binding.Q8_ERR_INVALID
+        assert fn(fake, fake, None, 4, 4, 4, None, None) == binding.Q8_ERR_INVALID
+        assert fn(odd, fake, fake, 4, 4, 4, None, None) == binding.Q8_ERR_INVALID
+        bad_corr = binding.Q8Epilogue(1.0, 0x1001)
+        assert fn(fake, fake, fake, 4, 4, 4, ctypes.byref(bad_corr), None) == binding.Q8_ERR_INVALID
+        # (M + 128) * (K + 32) must stay below 2^30 (32-bit byte offsets with one tile of overhang)
+        assert fn(fake, fake, fake, 1 << 20, 1 << 10, 4, None, None) == binding.Q8_ERR_TOO_LARGE
+        assert fn(fake, fake, fake, 4, 1 << 10, 1 << 20, None, None) == binding.Q8_ERR_TOO_LARGE
+        # empty outputs are a no-op
+        assert fn(None, None, None, 0, 7, 5, None, None) == binding.Q8_OK
+        assert fn(None, None, None, 3, 7, 0, None, None) == binding.Q8_OK
+
+
 def test_release_without_work_is_safe():
     binding.q8_release()
