@@ -35,6 +35,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E peak
 F32_MFMA_PEAK_TFLOPS = 157.3  # MI355X published dense f32 matrix peak
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
+# The dense f32 products run on the bf16 matrix cores: every f32 product is
+# six bf16 part products (an exact three-part split of each operand).
+DENSE_BF16_PRODUCTS = 6
 CSRC = os.path.join(ROOT, "quantized_decode_gemv_q8_amd", "csrc")
 # Sources whose hash stamps a traffic measurement (the kernel code itself).
 KERNEL_SRC = (os.path.join(CSRC, "q8_gemv_kernel.h"), os.path.join(CSRC, "q8_common.h"))
@@ -424,6 +428,12 @@ def main():
     }
     if unfused is not None:
         result["unfused"] = unfused
+    if dense:
+        # Hardware view of the same launches: bf16 MFMA flops issued against the bf16 peak.
+        issued = DENSE_BF16_PRODUCTS * achieved
+        result["bf16_mfma_issue"] = {"achieved": round(issued, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(issued / BF16_MFMA_PEAK_TFLOPS, 4),
+                                     "bf16_products_per_f32_product": DENSE_BF16_PRODUCTS}
     if not args.no_cpu_baseline and wl.op == "q8":
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, A0, W0, S0)

@@ -200,12 +200,16 @@ q8_status q8_dot_t(const int8_t *A, const int8_t *W, int32_t *C,
  *      must not alias A or B
  *   epilogue  host pointer, or NULL for alpha = 1 and no corr (an attention
  *      score tile is dot_t with alpha = 1/sqrt(head dim))
- * f32 operands and f32 accumulation (full f32 products on the matrix cores,
- * no operand rounding); each output is rounded as fmaf(corr[m], C_old,
- * alpha * P).  Any M, K, N >= 0; every pointer 4-byte aligned; rows whose
- * starts are all 16-byte aligned (K % 4 == 0, and N % 4 == 0 for q8_dot_f32,
- * with 16-byte aligned A and B) take wider loads.  K == 0 gives a zero
- * product.  Deterministic: the summation order depends only on K.
+ * f32 operands and f32 accumulation: each operand is split exactly into three
+ * bf16 parts and the six largest part products are accumulated in f32 on the
+ * bf16 matrix cores (the three dropped ones are below 2^-24 |a b| together),
+ * so the products keep f32 accuracy; each output is rounded as
+ * fmaf(corr[m], C_old, alpha * P).  Any M, K, N >= 0; every pointer 4-byte
+ * aligned; when K % 4 == 0 and A and B are 16-byte aligned (and N % 4 == 0
+ * for q8_dot_f32), the k-contiguous operands take 16-byte loads.  Operands
+ * below about 2^-110 in magnitude may lose their low parts to denormal
+ * handling.  K == 0 gives a zero product.  Deterministic: the summation order
+ * depends only on K.
  * Errors: Q8_ERR_INVALID (negative extent, NULL or misaligned pointer),
  * Q8_ERR_TOO_LARGE ((M + 128) * (K + 32) or (N + 128) * (K + 32) at or above
  * 2^30, or M * N at or above 2^31), Q8_ERR_UNSUPPORTED_DEVICE, Q8_ERR_HIP.

@@ -5,41 +5,49 @@
 // Operation: "dot and tensor cores" page, table of built-ins (dot(a, b) is
 // a @ b, dot_t(a, b) is a @ b^T), section "The k loop" (a workgroup owns an
 // output tile and adds the product of one panel of A and one of B per step of
-// K; under pipelining the copy of the next panel overlaps the math on the
-// current one) and section "The fused epilogue" (the product is scaled, and
-// optionally added to row-scaled old contents, as it is written).
+// K, the copy of the next panel overlapping the math on the current one) and
+// section "The fused epilogue" (the product is scaled, and optionally added to
+// row-scaled old contents, as it is written).
 //
-// Precision.  Section "Hardware paths" gives f32 operands an f32 accumulator
-// on FMA units.  v_mfma_f32_32x32x2_f32 multiplies full f32 operands into an
-// f32 accumulator (no operand rounding), so it keeps that contract; it is
-// also the only way to reach the chip's f32 matrix rate, since vector FMA
-// without packed instructions gets half of it.
+// Precision.  Section "Hardware paths" gives f32 operands an f32 accumulator;
+// tensor-core paths that round the operands to 16 bits would miss that.  Here
+// every f32 operand is split exactly into three bf16 parts, x = x0 + x1 + x2
+// (each part the round-to-nearest bf16 of what the previous ones leave; the
+// subtractions are exact and 3 x 8 significant bits hold all 24 of an f32),
+// and of the nine part products the six with p + q <= 2 are accumulated in
+// f32 by v_mfma_f32_16x16x32_bf16.  The three dropped products are below
+// 2^-24 |a b| together, so every product keeps f32 accuracy while the work
+// runs on the bf16 matrix cores: six bf16 MFMAs per f32 product still beat
+// the f32 matrix rate (measured 199 against 129 TFLOP/s of f32 products on
+// a 4096^3 product).
 //
 // Work decomposition (gfx950):
 //   * A workgroup of four wave64s owns a 128 x 128 tile of C; wave w owns the
-//     64 x 64 quarter (w / 2, w % 2) as 2 x 2 MFMA tiles of 32 x 32 (64
-//     accumulator registers per lane).
-//   * K is walked in panels of 32.  Panel p + 1 is loaded from global memory
-//     into registers while panel p is multiplied out of LDS; the registers
-//     are then written to the other LDS buffer and one barrier per panel
-//     separates the two (two LDS buffers).
-//   * Within a panel, MFMA step s (0..15) takes k = s from lanes 0..31 and
-//     k = 16 + s from lanes 32..63 (the contraction is a sum, so any pairing
-//     of k with MFMA slots that both operands share is the same product up to
-//     rounding order).  A lane therefore reads 16 consecutive k of its row of
-//     a [row][k] tile as four 16-byte LDS reads.
-//   * LDS tiles: A and dot_t's B as [128 rows][32 k] with a row pitch of 36
-//     floats (8 consecutive rows of 144 bytes start on distinct 4-bank groups,
-//     so 16-byte reads of 8 lanes never share a bank); dot's B as [32 k][128
-//     columns] with a pitch of 132 floats, read one dword per lane (32 lanes
-//     read 128 contiguous bytes).
+//     64 x 64 quarter (w / 2, w % 2) as 4 x 4 MFMA tiles of 16 x 16 (64
+//     accumulator registers per lane).  K goes in panels of 32, one MFMA
+//     k-slice.
+//   * Each thread loads its share of the next panel (A, and B) into registers
+//     while the current one is multiplied; the panel is split as it is
+//     written to LDS, as three bf16 part tiles [row][k].  One LDS buffer
+//     (60 KB) lets two workgroups share a CU, with two barriers per panel;
+//     the MFMA block runs at raised wave priority so the other workgroup's
+//     staging fills its gaps.
+//   * LDS padding ("@padstage"): the part tiles are read by column (the 16
+//     lanes of a read pass take 16 rows at the same k), so rows are padded
+//     from 64 to 96 bytes.  Measured against the unpadded tile, the padding
+//     takes the 4096^3 product from 832 to 678 us; a pad of 16 bytes (the
+//     pages' 8 elements) gives 690.
+//   * Loads keep a per-lane offset fixed for the whole K loop; the panel's k
+//     offset and every row step are scalar offsets.  dot's B [K,N] is read
+//     with dword loads so that each thread holds four consecutive k of one
+//     column (its [column][k] part tiles are then written 8 bytes at a time).
 //   * Tiles are dealt to the eight XCDs in contiguous ranges (the dispatcher
 //     sends workgroup i to XCD i mod 8), and inside a range in groups of
 //     eight tile rows, column by column, so that the workgroups resident on
 //     one XCD share panels of A and B in its L2.
 //   * Ragged M and N are masked at the store; a ragged last panel of K is
-//     zero-filled before it reaches LDS.  Rows and columns past the operands
-//     are read through bounded buffer descriptors (reads past the end return
+//     zero-filled as it is staged.  Rows and columns past the operands are
+//     read through bounded buffer descriptors (reads past the end return
 //     zero, nothing faults).
 #include <type_traits>
 
@@ -49,15 +57,10 @@ namespace q8 {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
-typedef float f16v __attribute__((ext_vector_type(16)));
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTM = 128;            // rows of C per workgroup
 constexpr int kTN = 128;            // columns of C per workgroup
-constexpr int kTK = 32;             // K per panel
-constexpr int kPitchK = kTK + 4;    // [row][k] tile pitch, floats
-constexpr int kPitchN = kTN + 4;    // [k][column] tile pitch, floats
-constexpr int kRowTile = kTM * kPitchK;  // floats of one [128][32] tile
+constexpr int kTK = 32;             // K per panel (one MFMA k-slice)
 constexpr int kGroupRows = 8;       // tile rows per group of the tile order
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
@@ -82,87 +85,10 @@ struct SFor {
 };
 
 // Registers of one thread's share of a 128 x 32 panel (4096 floats over 256
-// threads): four 16-byte chunks at VEC 4, sixteen dwords at VEC 1.
+// threads).
 struct Panel {
   f4 v[4];
 };
-
-// Loads this thread's share of a k-contiguous panel: rows row0..row0+127 of
-// a [rows][K] matrix (row pitch K floats), columns k0..k0+31.
-//   VEC 4: chunk c = tid + 256 i is row c / 8, k 4 (c % 8).
-//   VEC 1: element e = tid + 256 j is row e / 32, k e % 32.
-template <int VEC>
-__device__ __forceinline__ void load_rows(Panel &pn, __amdgpu_buffer_rsrc_t rs, int tid, int row0, int K, int k0) {
-  if constexpr (VEC == 4) {
-    const uint32_t base = ((uint32_t)(row0 + tid / 8) * (uint32_t)K + (uint32_t)(k0 + 4 * (tid % 8))) * 4u;
-    const uint32_t step = 32u * (uint32_t)K * 4u;
-    SFor<0, 4>::run([&](auto i) {
-      pn.v[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + i * step, 0u, 0));
-    });
-  } else {
-    const uint32_t base = ((uint32_t)(row0 + tid / 32) * (uint32_t)K + (uint32_t)(k0 + tid % 32)) * 4u;
-    const uint32_t step = 8u * (uint32_t)K * 4u;
-    SFor<0, 16>::run([&](auto j) {
-      pn.v[j / 4][j % 4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, base + j * step, 0u, 0));
-    });
-  }
-}
-
-// Writes a k-contiguous panel to a [128][kPitchK] LDS tile, zeroing k >= kv.
-template <int VEC>
-__device__ __forceinline__ void store_rows(float *t, const Panel &pn, int tid, int kv) {
-  if constexpr (VEC == 4) {
-    const int kc = 4 * (tid % 8);
-    const bool live = kc < kv;  // K % 4 == 0 at VEC 4: a chunk is all in or all out
-    SFor<0, 4>::run([&](auto i) {
-      const f4 x = live ? pn.v[i] : f4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f4 *>(t + (tid / 8 + 32 * i) * kPitchK + kc) = x;
-    });
-  } else {
-    const int k = tid % 32;
-    const bool live = k < kv;
-    SFor<0, 16>::run([&](auto j) {
-      t[(tid / 32 + 8 * j) * kPitchK + k] = live ? pn.v[j / 4][j % 4] : 0.f;
-    });
-  }
-}
-
-// Loads this thread's share of a [32 k][128 columns] panel of dot's B [K,N].
-//   VEC 4: chunk c = tid + 256 i is k c / 32, column 4 (c % 32).
-//   VEC 1: element e = tid + 256 j is k e / 128, column e % 128.
-template <int VEC>
-__device__ __forceinline__ void load_cols(Panel &pn, __amdgpu_buffer_rsrc_t rs, int tid, int k0, int N, int n0) {
-  if constexpr (VEC == 4) {
-    const uint32_t base = ((uint32_t)(k0 + tid / 32) * (uint32_t)N + (uint32_t)(n0 + 4 * (tid % 32))) * 4u;
-    const uint32_t step = 8u * (uint32_t)N * 4u;
-    SFor<0, 4>::run([&](auto i) {
-      pn.v[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + i * step, 0u, 0));
-    });
-  } else {
-    const uint32_t base = ((uint32_t)(k0 + tid / 128) * (uint32_t)N + (uint32_t)(n0 + tid % 128)) * 4u;
-    const uint32_t step = 2u * (uint32_t)N * 4u;
-    SFor<0, 16>::run([&](auto j) {
-      pn.v[j / 4][j % 4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, base + j * step, 0u, 0));
-    });
-  }
-}
-
-// Writes dot's B panel to a [32][kPitchN] LDS tile, zeroing k >= kv.
-template <int VEC>
-__device__ __forceinline__ void store_cols(float *t, const Panel &pn, int tid, int kv) {
-  if constexpr (VEC == 4) {
-    SFor<0, 4>::run([&](auto i) {
-      const int k = tid / 32 + 8 * i;
-      const f4 x = k < kv ? pn.v[i] : f4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f4 *>(t + k * kPitchN + 4 * (tid % 32)) = x;
-    });
-  } else {
-    SFor<0, 16>::run([&](auto j) {
-      const int k = tid / 128 + 2 * j;
-      t[k * kPitchN + tid % 128] = k < kv ? pn.v[j / 4][j % 4] : 0.f;
-    });
-  }
-}
 
 // Tile of this workgroup: XCD-contiguous ranges, then groups of kGroupRows
 // tile rows walked column by column.
@@ -178,17 +104,125 @@ __device__ __forceinline__ void tile_of(int wg, int n_wg, int tiles_m, int tiles
   *tn = r / rows;
 }
 
-// TRANS_B: dot_t (B [N,K]); otherwise dot (B [K,N]).  VEC: 4 when every row
-// of A and B starts 16-byte aligned, else 1.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+
+constexpr int kSP = kTK + 16;              // bf16 pitch of a [row][k] part tile (96 bytes)
+constexpr int kPartTile = 128 * kSP;       // bf16 elements of one part tile
+
+// Round-to-nearest-even bf16 of (x, y) packed into one dword, x in the low half.
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, y}, bf16x2));
+}
+
+// Splits four f32 into three bf16 parts each, as packed pairs: part q of
+// elements (2h, 2h+1) is dword h of out[q].  Each remainder is exact.
+__device__ __forceinline__ void split3(f4 x, u2 (&out)[3]) {
+  SFor<0, 2>::run([&](auto h) {
+    float a = x[2 * (int)h], b = x[2 * (int)h + 1];
+    SFor<0, 3>::run([&](auto q) {
+      const uint32_t u = pk_bf16(a, b);
+      out[q][(int)h] = u;
+      if constexpr (q < 2) {
+        a -= __uint_as_float(u << 16);
+        b -= __uint_as_float(u & 0xffff0000u);
+      }
+    });
+  });
+}
+
+// Loads of the split kernel: the per-lane part of each address is fixed for
+// the whole K loop, and the panel's k offset and each row step go into the
+// scalar offset.
+//   rows  (A, and dot_t's B): VEC 4: chunk i is row tid/8 + 32 i, k 4 (tid % 8);
+//         VEC 1: element j is row tid/32 + 8 j, k tid % 32.
+//   cols  (dot's B [K,N]): element (j, e) is column tid % 128, k 4 (tid/128 + 2 j) + e.
+template <int VEC>
+__device__ __forceinline__ uint32_t rows_voff(int tid, int row0, int K) {
+  return VEC == 4 ? ((uint32_t)(row0 + tid / 8) * (uint32_t)K + 4u * (uint32_t)(tid % 8)) * 4u
+                  : ((uint32_t)(row0 + tid / 32) * (uint32_t)K + (uint32_t)(tid % 32)) * 4u;
+}
+template <int VEC>
+__device__ __forceinline__ void sload_rows(Panel &pn, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int K, int k0) {
+  if constexpr (VEC == 4) {
+    SFor<0, 4>::run([&](auto i) {
+      const uint32_t so = (uint32_t)k0 * 4u + (uint32_t)(32 * i) * (uint32_t)K * 4u;
+      pn.v[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, so, 0));
+    });
+  } else {
+    SFor<0, 16>::run([&](auto j) {
+      const uint32_t so = (uint32_t)k0 * 4u + (uint32_t)(8 * j) * (uint32_t)K * 4u;
+      pn.v[j / 4][j % 4] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, so, 0));
+    });
+  }
+}
+__device__ __forceinline__ uint32_t cols_voff(int tid, int n0, int N) {
+  return ((uint32_t)(4 * (tid / 128)) * (uint32_t)N + (uint32_t)(n0 + tid % 128)) * 4u;
+}
+__device__ __forceinline__ void sload_cols(Panel &pn, __amdgpu_buffer_rsrc_t rs, uint32_t voff, int N, int k0) {
+  SFor<0, 4>::run([&](auto j) {
+    SFor<0, 4>::run([&](auto e) {
+      const uint32_t so = (uint32_t)(k0 + 8 * j + e) * (uint32_t)N * 4u;
+      pn.v[j][(int)e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, so, 0));
+    });
+  });
+}
+
+// Writes a rows panel as three [128][kSP] part tiles.  MASK zeroes k >= kv
+// (only the ragged last panel needs it).
+template <int VEC, bool MASK>
+__device__ __forceinline__ void stage_rows_split(__bf16 *t, const Panel &pn, int tid, int kv) {
+  if constexpr (VEC == 4) {
+    const int kc = 4 * (tid % 8);
+    SFor<0, 4>::run([&](auto i) {
+      u2 q[3];
+      split3(MASK && kc >= kv ? f4{0.f, 0.f, 0.f, 0.f} : pn.v[i], q);
+      const int off = (tid / 8 + 32 * i) * kSP + kc;
+      SFor<0, 3>::run([&](auto pp) { *reinterpret_cast<u2 *>(t + pp * kPartTile + off) = q[pp]; });
+    });
+  } else {
+    const int k = tid % 32;
+    SFor<0, 4>::run([&](auto i) {
+      u2 q[3];
+      split3(MASK && k >= kv ? f4{0.f, 0.f, 0.f, 0.f} : pn.v[i], q);
+      SFor<0, 4>::run([&](auto e) {
+        const int off = (tid / 32 + 8 * (4 * i + e)) * kSP + k;
+        SFor<0, 3>::run([&](auto pp) {
+          const uint32_t w = q[pp][(int)e / 2];
+          reinterpret_cast<uint16_t *>(t)[pp * kPartTile + off] = (uint16_t)(e % 2 ? w >> 16 : w);
+        });
+      });
+    });
+  }
+}
+
+// Writes dot's B panel (cols layout) as three [128 columns][kSP] part tiles.
+template <bool MASK>
+__device__ __forceinline__ void stage_cols_split(__bf16 *t, const Panel &pn, int tid, int kv) {
+  SFor<0, 4>::run([&](auto j) {
+    const int kq = 4 * (tid / 128 + 2 * j);
+    f4 x = pn.v[j];
+    if constexpr (MASK) {
+      SFor<0, 4>::run([&](auto e) { x[(int)e] = kq + (int)e < kv ? x[(int)e] : 0.f; });
+    }
+    u2 q[3];
+    split3(x, q);
+    const int off = (tid % 128) * kSP + kq;
+    SFor<0, 3>::run([&](auto pp) { *reinterpret_cast<u2 *>(t + pp * kPartTile + off) = q[pp]; });
+  });
+}
+
 template <bool TRANS_B, int VEC>
-__global__ __launch_bounds__(kThreads) void dense_f32_kernel(DenseArgs p) {
-  __shared__ __attribute__((aligned(16))) float a_lds[2][kRowTile];
-  __shared__ __attribute__((aligned(16))) float b_lds[2][TRANS_B ? kRowTile : kTK * kPitchN];
+__global__ __launch_bounds__(kThreads) void dense_split_kernel(DenseArgs p) {
+  __shared__ __attribute__((aligned(16))) __bf16 a_lds[3 * kPartTile];
+  __shared__ __attribute__((aligned(16))) __bf16 b_lds[3 * kPartTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int r32 = lane & 31, half = lane >> 5;
+  const int c16 = lane & 15, g4 = lane >> 4;
   const int tiles_m = (p.M + kTM - 1) / kTM, tiles_n = (p.N + kTN - 1) / kTN;
   int tm, tn;
   tile_of(blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, &tm, &tn);
@@ -198,92 +232,90 @@ __global__ __launch_bounds__(kThreads) void dense_f32_kernel(DenseArgs p) {
   const __amdgpu_buffer_rsrc_t b_rs = rsrc(p.B, (uint32_t)p.N * (uint32_t)p.K * 4u);
   const int np = (p.K + kTK - 1) / kTK;
 
+  const uint32_t a_voff = rows_voff<VEC>(tid, m0, p.K);
+  const uint32_t b_voff = TRANS_B ? rows_voff<VEC>(tid, n0, p.K) : cols_voff(tid, n0, p.N);
   auto load = [&](Panel &pa, Panel &pb, int kt) {
-    load_rows<VEC>(pa, a_rs, tid, m0, p.K, kt);
+    sload_rows<VEC>(pa, a_rs, a_voff, p.K, kt);
     if constexpr (TRANS_B) {
-      load_rows<VEC>(pb, b_rs, tid, n0, p.K, kt);
+      sload_rows<VEC>(pb, b_rs, b_voff, p.K, kt);
     } else {
-      load_cols<VEC>(pb, b_rs, tid, kt, p.N, n0);
+      sload_cols(pb, b_rs, b_voff, p.N, kt);
     }
   };
-  auto store = [&](const Panel &pa, const Panel &pb, int buf, int kt) {
-    const int kv = p.K - kt;
-    store_rows<VEC>(a_lds[buf], pa, tid, kv);
+  auto stage = [&](auto mask_, const Panel &pa, const Panel &pb, int kv) {
+    constexpr bool MASK = decltype(mask_)::value;
+    stage_rows_split<VEC, MASK>(a_lds, pa, tid, kv);
     if constexpr (TRANS_B) {
-      store_rows<VEC>(b_lds[buf], pb, tid, kv);
+      stage_rows_split<VEC, MASK>(b_lds, pb, tid, kv);
     } else {
-      store_cols<VEC>(b_lds[buf], pb, tid, kv);
+      stage_cols_split<MASK>(b_lds, pb, tid, kv);
     }
   };
 
-  f16v acc[2][2];
-  SFor<0, 2>::run([&](auto i) { SFor<0, 2>::run([&](auto j) { acc[i][j] = f16v{}; }); });
+  f4 acc[4][4];
+  SFor<0, 4>::run([&](auto i) { SFor<0, 4>::run([&](auto j) { acc[i][j] = f4{0.f, 0.f, 0.f, 0.f}; }); });
 
   Panel pa, pb;
   load(pa, pb, 0);
-  store(pa, pb, 0, 0);
-  lds_barrier();
-
   for (int pnl = 0; pnl < np; ++pnl) {
-    const int buf = pnl & 1;
-    const bool more = pnl + 1 < np;
-    if (more) load(pa, pb, (pnl + 1) * kTK);
+    const int kt = pnl * kTK;
+    if (pnl > 0) lds_barrier();  // every wave has finished reading the previous panel
+    if (p.K - kt >= kTK) {
+      stage(std::false_type{}, pa, pb, kTK);
+    } else {
+      stage(std::true_type{}, pa, pb, p.K - kt);
+    }
+    lds_barrier();
+    if (pnl + 1 < np) load(pa, pb, kt + kTK);
 
-    // Operands of this panel: lane (r32, half) holds k = 16 half + s, s = 0..15.
-    f4 af[2][4], bf[2][4];
-    SFor<0, 2>::run([&](auto i) {
-      const float *src = a_lds[buf] + (64 * wm + 32 * i + r32) * kPitchK + 16 * half;
-      SFor<0, 4>::run([&](auto q) { af[i][q] = *reinterpret_cast<const f4 *>(src + 4 * q); });
+    // Lane l of MFMA tile (i, j) supplies row / column 16 i + l % 16 and
+    // k = 8 (l / 16) .. +7 of each part.
+    bf16x8 af[4][3], bf[4][3];
+    SFor<0, 4>::run([&](auto i) {
+      SFor<0, 3>::run([&](auto pp) {
+        af[i][pp] = *reinterpret_cast<const bf16x8 *>(a_lds + pp * kPartTile + (64 * wm + 16 * i + c16) * kSP + 8 * g4);
+        bf[i][pp] = *reinterpret_cast<const bf16x8 *>(b_lds + pp * kPartTile + (64 * wn + 16 * i + c16) * kSP + 8 * g4);
+      });
     });
-    SFor<0, 2>::run([&](auto j) {
-      if constexpr (TRANS_B) {
-        const float *src = b_lds[buf] + (64 * wn + 32 * j + r32) * kPitchK + 16 * half;
-        SFor<0, 4>::run([&](auto q) { bf[j][q] = *reinterpret_cast<const f4 *>(src + 4 * q); });
-      } else {
-        const float *src = b_lds[buf] + (16 * half) * kPitchN + 64 * wn + 32 * j + r32;
-        SFor<0, 16>::run([&](auto s) { bf[j][s / 4][s % 4] = src[s * kPitchN]; });
-      }
-    });
-    SFor<0, 16>::run([&](auto s) {
-      SFor<0, 2>::run([&](auto i) {
-        SFor<0, 2>::run([&](auto j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][s / 4][s % 4], bf[j][s / 4][s % 4], acc[i][j], 0,
-                                                           0, 0);
+    // Part products with p + q <= 2, smallest first, at raised wave priority
+    // so that the other workgroup's staging fills the gaps rather than delays them.
+    __builtin_amdgcn_s_setprio(1);
+    SFor<0, 6>::run([&](auto t) {
+      constexpr int kP[6] = {2, 1, 0, 1, 0, 0};
+      constexpr int kQ[6] = {0, 1, 2, 0, 1, 0};
+      SFor<0, 4>::run([&](auto i) {
+        SFor<0, 4>::run([&](auto j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kP[t]], bf[j][kQ[t]], acc[i][j], 0, 0, 0);
         });
       });
     });
-
-    if (more) {
-      store(pa, pb, buf ^ 1, (pnl + 1) * kTK);
-      lds_barrier();
-    }
+    __builtin_amdgcn_s_setprio(0);
   }
 
-  // Epilogue.  Accumulator register r of lane (r32, half) in tile (i, j) is
-  // row 8 (r / 4) + 4 half + r % 4 and column r32 of that 32 x 32 tile.  A
-  // tile wholly inside C and an epilogue without row factors (both uniform
-  // over the workgroup) take straight-line stores.
+  // Lane l of tile (i, j) holds rows 16 i + 4 (l / 16) + e, column 16 j + l % 16.
+  // A tile wholly inside C without row factors (both uniform over the
+  // workgroup) takes straight-line stores.
   const bool whole = m0 + kTM <= p.M && n0 + kTN <= p.N;
-  const int m_w = m0 + 64 * wm + 4 * half, n_w = n0 + 64 * wn + r32;
+  const int m_w = m0 + 64 * wm + 4 * g4, n_w = n0 + 64 * wn + c16;
   if (whole && p.corr == nullptr) {
     float *base = p.C + (size_t)m_w * p.N + n_w;
-    SFor<0, 2>::run([&](auto i) {
-      SFor<0, 2>::run([&](auto j) {
-        SFor<0, 16>::run([&](auto r) {
-          base[(size_t)(32 * i + 8 * (r / 4) + r % 4) * p.N + 32 * j] = p.alpha * acc[i][j][(int)r];
+    SFor<0, 4>::run([&](auto i) {
+      SFor<0, 4>::run([&](auto j) {
+        SFor<0, 4>::run([&](auto e) {
+          base[(size_t)(16 * i + e) * p.N + 16 * j] = p.alpha * acc[i][j][(int)e];
         });
       });
     });
     return;
   }
-  SFor<0, 2>::run([&](auto i) {
-    SFor<0, 2>::run([&](auto j) {
-      const int n = n_w + 32 * j;
-      SFor<0, 16>::run([&](auto r) {
-        const int m = m_w + 32 * i + 8 * (r / 4) + r % 4;
+  SFor<0, 4>::run([&](auto i) {
+    SFor<0, 4>::run([&](auto j) {
+      const int n = n_w + 16 * j;
+      SFor<0, 4>::run([&](auto e) {
+        const int m = m_w + 16 * i + e;
         if (m < p.M && n < p.N) {
           float *c = p.C + (size_t)m * p.N + n;
-          float y = p.alpha * acc[i][j][(int)r];
+          float y = p.alpha * acc[i][j][(int)e];
           if (p.corr) y = fmaf(p.corr[m], *c, y);
           *c = y;
         }
@@ -299,15 +331,15 @@ hipError_t launch_dense_f32(const DenseArgs &a, bool trans_b, int vec, hipStream
   const dim3 grid((unsigned)tiles), block(kThreads);
   if (vec == 4) {
     if (trans_b) {
-      hipLaunchKernelGGL((dense_f32_kernel<true, 4>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((dense_split_kernel<true, 4>), grid, block, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((dense_f32_kernel<false, 4>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((dense_split_kernel<false, 4>), grid, block, 0, stream, a);
     }
   } else if (vec == 1) {
     if (trans_b) {
-      hipLaunchKernelGGL((dense_f32_kernel<true, 1>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((dense_split_kernel<true, 1>), grid, block, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((dense_f32_kernel<false, 1>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((dense_split_kernel<false, 1>), grid, block, 0, stream, a);
     }
   } else {
     return hipErrorInvalidValue;

@@ -3,10 +3,13 @@
 
 Bar: max over outputs of |C_gpu - y_oracle| / D <= 1e-5, where D is
 |alpha| * sum_k |A B| + |corr[m] * C_old[m,n]| (the oracle's normaliser);
-D == 0 requires an exact zero.  f32 accumulation of K products has a rounding
-error below about K * 2^-24 * D in the worst case and near sqrt(K) * 2^-24 * D
-for these inputs, far inside the bar; integer-valued inputs whose sums stay
-below 2^24 are exact and are compared bit for bit.
+D == 0 requires an exact zero.  The GPU forms each product from an exact
+three-part bf16 split of both operands, dropping the three smallest part
+products (together below 2^-24 |a b|), and accumulates in f32: the error
+stays below about K * 2^-23 * D in the worst case and near sqrt(K) * 2^-24 * D
+for these inputs, far inside the bar.  Integer-valued inputs whose sums stay
+below 2^24 are exact (their high parts hold them whole) and are compared bit
+for bit.
 """
 
 import ctypes
@@ -113,6 +116,17 @@ def test_epilogue(transposed):
     # alpha == 0 leaves one rounding of corr * old
     C0 = gpu_dense(A, B, transposed, 0.0, corr, old)
     assert np.array_equal(C0, (corr[:, None].astype(np.float64) * old.astype(np.float64)).astype(np.float32))
+
+
+@pytest.mark.parametrize("transposed", [False, True])
+def test_wide_dynamic_range(transposed):
+    # operands spanning 2^-20 .. 2^20 with mixed signs: every part of the split matters
+    rng = np.random.default_rng(410)
+    M, K, N = 96, 700, 130
+    A = (rng.standard_normal((M, K)) * 2.0 ** rng.integers(-20, 21, (M, K))).astype(np.float32)
+    shape = (N, K) if transposed else (K, N)
+    B = (rng.standard_normal(shape) * 2.0 ** rng.integers(-20, 21, shape)).astype(np.float32)
+    assert_parity(A, B, transposed, gpu_dense(A, B, transposed))
 
 
 def test_power_of_two_scale_is_exact():
