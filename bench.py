@@ -47,7 +47,7 @@ GEMM_SRC = (os.path.join(CSRC, "q8_gemm.hip"), os.path.join(CSRC, "q8_common.h")
 DENSE_SRC = (os.path.join(CSRC, "dense_f32.hip"), os.path.join(CSRC, "q8_common.h"))
 # Kernel-name prefix of each source set, as rocprofv3 reports it.
 KERNEL_NAMES = {KERNEL_SRC: "q8_gemv_kernel", GEMM_SRC: "q8_gemm_kernel", DOT_SRC: "dot_t_",
-                DENSE_SRC: "dense_f32_kernel"}
+                DENSE_SRC: "dense_split_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 # Rotated copies per workload: enough to exceed the Infinity Cache (>= 1 GiB).
