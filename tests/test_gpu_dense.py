@@ -58,6 +58,15 @@ def test_dense_parity(M, K, N, transposed):
     assert_parity(A, B, transposed, gpu_dense(A, B, transposed))
 
 
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 31, 32, 33, 63, 64, 65, 96, 97, 127])
+def test_panel_edges(K):
+    # K around the 32-wide panels (4-byte and 16-byte load paths), M and N around the 128 tile
+    for M, N in ((127, 129), (129, 128), (1, 256)):
+        for tr in (False, True):
+            A, B = workloads.dense_inputs(M, K, N, (411, M, K, N, tr), tr)
+            assert_parity(A, B, tr, gpu_dense(A, B, tr))
+
+
 @pytest.mark.parametrize("name", ["dot_f32_4096", "scores_4096x4096_d128"])
 def test_dense_full_size_sampled_rows(name):
     wl = workloads.WORKLOADS[name]
