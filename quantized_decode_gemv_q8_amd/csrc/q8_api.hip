@@ -205,8 +205,17 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   if (pl.kind != 0 && pl.kind != Q8_PLAN_STREAM && pl.kind != Q8_PLAN_MATRIX) return Q8_ERR_INVALID;
   const bool matrix_fits = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 && N % 16 == 0 &&
                            w_align % 16 == 0 && s_align % 16 == 0;
+  // Automatic choice.  The matrix-core product has a floor of about 16 us (its
+  // split combine), so for up to 4 rows of a small weight matrix the per-row
+  // stream is faster (K = N = 4096: 12.0 / 14.6 us at 2 / 4 rows against 17.5
+  // / 17.8); from 5 rows, or once W is large, the matrix cores win (K = N =
+  // 4096, 8 rows: 18.2 against 26.3 us; K = 8192, N = 28672, 2 rows: 50.2
+  // against 56.9 us).
+  constexpr int64_t kMatrixSmallRowsMinWeights = (int64_t)1 << 26;
+  const bool matrix_pays = M >= 5 || K * N >= kMatrixSmallRowsMinWeights;
   if (pl.kind == 0)
-    pl.kind = (matrix_fits && M >= Q8_MATRIX_MIN_ROWS && pl.vec == 0 && pl.m_tile == 0 && pl.workgroups == 0)
+    pl.kind = (matrix_fits && matrix_pays && M >= Q8_MATRIX_MIN_ROWS && pl.vec == 0 && pl.m_tile == 0 &&
+               pl.workgroups == 0)
                   ? Q8_PLAN_MATRIX
                   : Q8_PLAN_STREAM;
   if (pl.kind == Q8_PLAN_MATRIX) {

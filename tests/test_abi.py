@@ -95,6 +95,11 @@ def test_plan_kind_follows_rows_and_layout():
     assert plan(65, 8192, 28672)["kind"] == binding.PLAN_STREAM    # above it
     assert plan(16, 8192, 5000)["kind"] == binding.PLAN_STREAM     # N % 16 != 0
     assert plan(16, 8192, 4096, w_align=8)["kind"] == binding.PLAN_STREAM
+    # up to 4 rows of a small W stay on the stream; 5 rows or a large W go to the matrix cores
+    assert plan(4, 4096, 4096)["kind"] == binding.PLAN_STREAM
+    assert plan(2, 4096, 4096)["kind"] == binding.PLAN_STREAM
+    assert plan(5, 4096, 4096)["kind"] == binding.PLAN_MATRIX
+    assert plan(3, 8192, 28672)["kind"] == binding.PLAN_MATRIX
     assert plan(16, 8192, 28672)["workgroups"] == 56 * 8          # two workgroups per CU up to 16 rows
     assert plan(32, 8192, 28672)["workgroups"] == 56 * 4          # one above
     assert plan(64, 8192, 28672)["workgroups"] == 56 * 4          # per 32-row pass
