@@ -90,7 +90,7 @@ def test_plan_kind_follows_rows_and_layout():
     assert plan(1, 64, 4096)["kind"] == binding.PLAN_STREAM        # one row: the matvec
     assert plan(2, 8192, 28672)["kind"] == binding.PLAN_MATRIX
     assert plan(32, 8192, 28672)["kind"] == binding.PLAN_MATRIX
-    assert plan(33, 8192, 28672)["kind"] == binding.PLAN_MATRIX    # two 32-row passes
+    assert plan(33, 8192, 28672)["kind"] == binding.PLAN_MATRIX    # the 64-row instance
     assert plan(64, 8192, 28672)["kind"] == binding.PLAN_MATRIX
     assert plan(65, 8192, 28672)["kind"] == binding.PLAN_STREAM    # above it
     assert plan(16, 8192, 5000)["kind"] == binding.PLAN_STREAM     # N % 16 != 0
@@ -102,7 +102,7 @@ def test_plan_kind_follows_rows_and_layout():
     assert plan(3, 8192, 28672)["kind"] == binding.PLAN_MATRIX
     assert plan(16, 8192, 28672)["workgroups"] == 56 * 8          # two workgroups per CU up to 16 rows
     assert plan(32, 8192, 28672)["workgroups"] == 56 * 4          # one above
-    assert plan(64, 8192, 28672)["workgroups"] == 56 * 4          # per 32-row pass
+    assert plan(64, 8192, 28672)["workgroups"] == 56 * 4          # one workgroup per CU
     assert plan(16, 28672, 28672)["workgroups"] == 56 * 14       # at most 64 blocks per split
 
 
