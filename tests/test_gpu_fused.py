@@ -75,7 +75,8 @@ def test_fused_workloads(name):
 
 
 def test_single_sibling_matches_q8_matvec_bitwise():
-    for M, K, N, seed in [(1, 4096, 4096, 201), (4, 4100, 5000, 202)]:
+    # (16, 2048, 4096) takes the matrix cores on both entry points
+    for M, K, N, seed in [(1, 4096, 4096, 201), (4, 4100, 5000, 202), (16, 2048, 4096, 212)]:
         A, W, S = workloads.q8_inputs(M, K, N, seed)
         C = binding.q8_matvec(to_dev(A), to_dev(W), to_dev(S))
         torch.cuda.synchronize()
