@@ -131,6 +131,38 @@ def _blas_threads():
     return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def device_memory_info(dev_index):
+    """Memory clock and bus width as the HIP runtime reports them, and the peak
+    they imply.  HIP reports the HBM3/HBM3E clock at a quarter of the per-pin
+    data rate (MI300X: 1.3 GHz for 5.2 Gb/s pins, 5.3 TB/s), so the implied
+    peak is clock x 4 x bus bytes.  The published 8 TB/s stays the roofline
+    peak; this figure is reported beside it."""
+    import ctypes
+
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        clock, width = ctypes.c_int(0), ctypes.c_int(0)
+        # hipDeviceAttributeMemoryClockRate (kHz) and hipDeviceAttributeMemoryBusWidth (bits)
+        if hip.hipDeviceGetAttribute(ctypes.byref(clock), 60, dev_index) != 0 or \
+                hip.hipDeviceGetAttribute(ctypes.byref(width), 59, dev_index) != 0:
+            return None
+    except OSError:
+        return None
+    return {"memory_clock_khz": clock.value, "bus_width_bits": width.value,
+            "implied_peak_gbs": round(clock.value * 1e3 * 4 * width.value / 8 / 1e9, 1)}
+
+
 def cpu_baseline(wl, A, W, S, budget_s=12.0):
     """The oracle as it stands, timed on the host: whole-workload calls on copy 0,
     repeated until about `budget_s` seconds of CPU work have been measured."""
@@ -143,6 +175,7 @@ def cpu_baseline(wl, A, W, S, budget_s=12.0):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": _cpu_model(),
         "sample": f"f64 factored oracle on the whole M={wl.M} K={wl.K} N={wl.N} workload (copy 0), "
                   f"{n} calls in {total:.1f} s; BLAS threads {threads}, numpy upcasts single-threaded",
     }
@@ -163,6 +196,7 @@ def cpu_baseline_dense(wl, A, B, alpha, rows=512, budget_s=12.0):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": _cpu_model(),
         "sample": f"f64 dense oracle on rows 0..{As.shape[0] - 1} of A against all of B (K={wl.K} N={wl.N}, "
                   f"copy 0), {n} calls in {total:.1f} s; BLAS threads {threads}",
     }
@@ -426,6 +460,9 @@ def main():
                       "p10": round(float(np.percentile(per, 10)) * 1e3, 3),
                       "p90": round(float(np.percentile(per, 90)) * 1e3, 3)},
     }
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+                        **(device_memory_info(dev.index or 0) or {})}
     if unfused is not None:
         result["unfused"] = unfused
     if dense:
