@@ -17,8 +17,8 @@
  *   - All tensor pointers are DEVICE pointers (memory of the current HIP
  *     device) to dense row-major arrays; there are no leading-dimension
  *     arguments.  The caller owns them; the library only reads the inputs
- *     and overwrites the output (it never reads C).  C must not alias an
- *     input.
+ *     and overwrites the output.  It reads C only through an epilogue with
+ *     row factors (corr != NULL, below).  C must not alias an input.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls are asynchronous on that stream: a status of Q8_OK means the work
  *     was enqueued; faults surface at the caller's next synchronisation.
@@ -27,10 +27,12 @@
  *   - Sizes: every extent must be >= 0.  M == 0 or N == 0 is a no-op.  The
  *     library uses 32-bit element offsets, so K*N, M*K and M*N must each be
  *     below 2^31 (otherwise Q8_ERR_TOO_LARGE).
- *   - Thread safety: concurrent calls are safe on distinct streams.  The
- *     split-K workspace of q8_matvec is owned by the library, one per
- *     (device, stream); it is allocated on the first call that needs it on
- *     that stream (so that first call must not run under stream capture) and
+ *   - Thread safety: concurrent calls are safe on distinct streams.  Host
+ *     threads that share one stream must serialise their calls: a call that
+ *     needs a larger workspace frees the stream's smaller one.  The split-K
+ *     workspace of q8_matvec is owned by the library, one per (device,
+ *     stream); it is allocated on the first call that needs it on that
+ *     stream (so that first call must not run under stream capture) and
  *     freed by q8_release().
  */
 #ifndef Q8_GEMV_H

@@ -132,9 +132,32 @@ def _check_tensor(name, t, dtype, shape):
         raise ValueError(f"{name} must be contiguous (dense row-major)")
 
 
+def _check_disjoint(out_name, out, others):
+    """The library requires outputs that share no bytes with any other
+    argument; an overlap would be a silent race, so it is refused here."""
+    if out.numel() == 0:
+        return
+    a0 = out.data_ptr()
+    a1 = a0 + out.numel() * out.element_size()
+    for name, t in others:
+        if t is None or t.numel() == 0:
+            continue
+        b0 = t.data_ptr()
+        b1 = b0 + t.numel() * t.element_size()
+        if a0 < b1 and b0 < a1:
+            raise ValueError(f"{out_name} overlaps {name}")
+
+
+def _rank2(**named):
+    for name, t in named.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != 2:
+            raise ValueError(f"{name} must be rank 2, got {t.dim()} dimensions")
+
+
 def _q8_args(A, W, S, out):
-    if A.dim() != 2 or W.dim() != 2:
-        raise ValueError("A must be [M,K] and W [K,N]")
+    _rank2(A=A, W=W)
     M, K = A.shape
     N = W.shape[1]
     KB = (K + BLOCK - 1) // BLOCK
@@ -147,6 +170,7 @@ def _q8_args(A, W, S, out):
     for t in (W, S, out):
         if t.device != A.device:
             raise ValueError("all tensors must be on one device")
+    _check_disjoint("out", out, (("A", A), ("W", W), ("S", S)))
     return M, K, N, out
 
 
@@ -203,6 +227,10 @@ def q8_matvec_fused(A, Ws, Ss, outs=None, alpha=1.0, corr=None, plan=None, strea
         _check_tensor("corr", corr, torch.float32, (M,))
         if corr.device != A.device:
             raise ValueError("all tensors must be on one device")
+    inputs = [("corr", corr)] + [(f"Ws[{j}]", W) for j, W in enumerate(Ws)] + \
+        [(f"Ss[{j}]", S) for j, S in enumerate(Ss)]
+    for g, C in enumerate(res):
+        _check_disjoint(f"outs[{g}]", C, inputs + [(f"outs[{j}]", res[j]) for j in range(g)])
     sib = (Q8Sibling * n)(*[Q8Sibling(W.data_ptr(), S.data_ptr(), C.data_ptr()) for W, S, C in zip(Ws, Ss, res)])
     ep = Q8Epilogue(float(alpha), corr.data_ptr() if corr is not None else None)
     pl = ctypes.byref(_plan_struct(plan)) if plan is not None else None
@@ -226,8 +254,7 @@ def q8_matvec_choose_plan(M, K, N, w_align=256, s_align=256, num_cus=256):
 
 def q8_dot_t(A, W, out=None, stream=None):
     """C[m,n] = sum_k A[m,k] W[n,k] in exact i32 on the GPU; returns C (i32 [M,N])."""
-    if A.dim() != 2 or W.dim() != 2:
-        raise ValueError("A must be [M,K] and W [N,K]")
+    _rank2(A=A, W=W)
     M, K = A.shape
     N = W.shape[0]
     _check_tensor("A", A, torch.int8, (M, K))
@@ -237,6 +264,7 @@ def q8_dot_t(A, W, out=None, stream=None):
     _check_tensor("out", out, torch.int32, (M, N))
     if W.device != A.device or out.device != A.device:
         raise ValueError("all tensors must be on one device")
+    _check_disjoint("out", out, (("A", A), ("W", W)))
     with torch.cuda.device(A.device):
         st = load().q8_dot_t(A.data_ptr(), W.data_ptr(), out.data_ptr(), M, K, N,
                              _stream_handle(stream, A.device))
@@ -246,8 +274,7 @@ def q8_dot_t(A, W, out=None, stream=None):
 
 
 def _dense(name, A, B, transposed, out, alpha, corr, stream):
-    if A.dim() != 2 or B.dim() != 2:
-        raise ValueError("A and B must be rank 2")
+    _rank2(A=A, B=B)
     M, K = A.shape
     N = B.shape[0] if transposed else B.shape[1]
     _check_tensor("A", A, torch.float32, (M, K))
@@ -262,6 +289,7 @@ def _dense(name, A, B, transposed, out, alpha, corr, stream):
     for t in (B, out) + ((corr,) if corr is not None else ()):
         if t.device != A.device:
             raise ValueError("all tensors must be on one device")
+    _check_disjoint("out", out, (("A", A), ("B", B), ("corr", corr)))
     ep = Q8Epilogue(float(alpha), corr.data_ptr() if corr is not None else None)
     with torch.cuda.device(A.device):
         st = getattr(load(), name)(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, K, N, ctypes.byref(ep),

@@ -184,3 +184,31 @@ def test_dense_rejects_bad_extents_and_pointers():
 
 def test_release_without_work_is_safe():
     binding.q8_release()
+
+
+def test_binding_refuses_overlapping_outputs():
+    # host logic of the binding: byte ranges that share anything are refused
+    import torch
+
+    buf = torch.zeros(64, dtype=torch.float32)
+    a, b, c = buf[:16], buf[16:32], buf[8:24]
+    binding._check_disjoint("out", a, (("A", b), ("none", None), ("empty", buf[:0])))
+    for other in (c, buf, a):
+        with pytest.raises(ValueError, match="overlaps"):
+            binding._check_disjoint("out", a, (("A", other),))
+    # the last byte of one range and the first of the next do not overlap
+    raw = torch.zeros(32, dtype=torch.uint8)
+    binding._check_disjoint("out", raw[:16].view(torch.float32), (("W", raw[16:]),))
+    with pytest.raises(ValueError, match="overlaps"):
+        binding._check_disjoint("out", raw[:16].view(torch.float32), (("W", raw[15:]),))
+
+
+def test_binding_checks_types_and_ranks_before_the_device():
+    import torch
+
+    with pytest.raises(TypeError):
+        binding.q8_matvec([[1.0]], torch.zeros((1, 1), dtype=torch.int8), torch.zeros((1, 1)))
+    with pytest.raises(ValueError, match="rank 2"):
+        binding.q8_matvec(torch.zeros(4), torch.zeros((4, 1), dtype=torch.int8), torch.zeros((1, 1)))
+    with pytest.raises(ValueError, match="rank 2"):
+        binding.q8_dot_t_f32(torch.zeros((2, 2)), torch.zeros(2))

@@ -125,6 +125,21 @@ def test_invalid_plans_are_rejected():
 
 # ------------------------------------------------------------------ guards and edge cases
 
+def test_outputs_that_overlap_inputs_are_refused():
+    M, K, N = 2, 64, 32
+    A, W, S = (to_dev(x) for x in rand_q8(M, K, N, 106))
+    buf = torch.zeros(M * K + M * N, dtype=torch.float32, device=DEV)
+    buf[:M * K].copy_(A.flatten())
+    A_in = buf[:M * K].view(M, K)
+    with pytest.raises(ValueError, match="overlaps A"):
+        binding.q8_matvec(A_in, W, S, out=buf[M * K - 1:M * K - 1 + M * N].view(M, N))
+    binding.q8_matvec(A_in, W, S, out=buf[M * K:].view(M, N))  # adjacent, not overlapping
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError, match="overlaps outs"):
+        binding.q8_matvec_fused(A, [W, W], [S, S], outs=[C, C])
+    torch.cuda.synchronize()
+
+
 def test_canaries_and_full_overwrite():
     M, K, N = 3, 4100, 5000
     A, W, S = rand_q8(M, K, N, 105)
