@@ -33,7 +33,9 @@
  *     workspace of q8_matvec is owned by the library, one per (device,
  *     stream); it is allocated on the first call that needs it on that
  *     stream (so that first call must not run under stream capture) and
- *     freed by q8_release().
+ *     freed by q8_release().  Later calls on that stream may be captured
+ *     into a HIP graph and replayed: their arrival counters return to zero
+ *     inside every launch, and no call records a memset.
  */
 #ifndef Q8_GEMV_H
 #define Q8_GEMV_H

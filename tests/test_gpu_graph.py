@@ -1,0 +1,157 @@
+"""Every entry point captured in a HIP graph (torch.cuda.CUDAGraph) and
+replayed several times, with new inputs written eagerly between replays: each
+replay must equal an eager call on the same inputs bit for bit (the kernels
+are deterministic), and the first must meet the oracle's bar.
+
+The split-K counters re-arm themselves inside every launch, so a replayed
+launch finds them as an eager one does; the workspace is allocated by an
+eager call on the capture stream before capture begins (no allocation and no
+memset is recorded into the graph)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_decode_gemv_q8_amd import binding, workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-5
+REPLAYS = 4
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def replay_and_compare(call, outs, refresh, check_first):
+    """Warm up on a side stream, capture `call(outs)` there, then replay
+    REPLAYS times.  Before each replay `refresh(r)` writes new inputs in place
+    (eagerly); after it every output must equal an eager call's bitwise."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(outs)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(outs)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        refresh(r)
+        torch.cuda.synchronize()
+        print(f"[graph] replay {r}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        refs = [torch.empty_like(o) for o in outs]
+        with torch.cuda.stream(s):
+            call(refs)
+        s.synchronize()
+        for o, ref in zip(outs, refs):
+            assert torch.equal(o, ref), f"replay {r} differs from the eager call"
+        if r == 0:
+            check_first([o.cpu().numpy() for o in outs])
+    del g
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K,N,plan", [
+    (1, 4100, 5000, None),                 # stream path, ragged K and N, split-K combine
+    (3, 8192, 4096, {"workgroups": 256}),  # stream path, several rows per pass
+    (8, 1000, 1024, {"kind": binding.PLAN_MATRIX}),  # matrix cores, split combine
+])
+def test_q8_matvec_replays(M, K, N, plan):
+    A, W, S = workloads.q8_inputs(M, K, N, (500, M, K, N))
+    A_d, W_d, S_d = to_dev(A), to_dev(W), to_dev(S)
+    print(f"[graph] q8_matvec M={M} K={K} N={N} plan={plan}", flush=True)
+    rng = np.random.default_rng(501)
+    state = {"A": A}
+
+    def call(outs):
+        if plan is None:
+            binding.q8_matvec(A_d, W_d, S_d, out=outs[0])
+        else:
+            binding.q8_matvec_with_plan(A_d, W_d, S_d, plan, out=outs[0])
+
+    def refresh(r):
+        state["A"] = rng.standard_normal((M, K)).astype(np.float32)
+        A_d.copy_(to_dev(state["A"]))
+
+    def check_first(hosts):
+        err = oracle.normalised_error(hosts[0], oracle.q8_matvec(state["A"], W, S), oracle.q8_normaliser(state["A"], W, S))
+        assert err <= TOL, f"normalised error {err:.3e}"
+
+    replay_and_compare(call, [torch.empty((M, N), dtype=torch.float32, device=DEV)], refresh, check_first)
+
+
+def test_fused_siblings_replay():
+    M, K, N = 2, 2048, 3000
+    A, Ws, Ss = workloads.q8_fused_inputs(M, K, N, 3, (502, 0))
+    A_d = to_dev(A)
+    Ws_d, Ss_d = [to_dev(w) for w in Ws], [to_dev(s) for s in Ss]
+    print("[graph] q8_matvec_fused M=2 K=2048 N=3000 siblings=3 alpha=0.5", flush=True)
+    rng = np.random.default_rng(503)
+    state = {"A": A}
+
+    def call(outs):
+        binding.q8_matvec_fused(A_d, Ws_d, Ss_d, outs=outs, alpha=0.5)
+
+    def refresh(r):
+        state["A"] = rng.standard_normal((M, K)).astype(np.float32)
+        A_d.copy_(to_dev(state["A"]))
+
+    def check_first(hosts):
+        refs = oracle.q8_matvec_fused(state["A"], list(zip(Ws, Ss)), 0.5, None, None)
+        for g in range(3):
+            D = oracle.q8_fused_normaliser(state["A"], Ws[g], Ss[g], 0.5, None, None)
+            err = oracle.normalised_error(hosts[g], refs[g], D)
+            assert err <= TOL, f"sibling {g}: normalised error {err:.3e}"
+
+    outs = [torch.empty((M, N), dtype=torch.float32, device=DEV) for _ in range(3)]
+    replay_and_compare(call, outs, refresh, check_first)
+
+
+def test_dot_t_replay():
+    M, K, N = 16, 4096, 1024
+    A, W = workloads.dot_t_inputs(M, K, N, (504, 0))
+    A_d, W_d = to_dev(A), to_dev(W)
+    print("[graph] q8_dot_t M=16 K=4096 N=1024", flush=True)
+    rng = np.random.default_rng(505)
+    state = {"A": A}
+
+    def call(outs):
+        binding.q8_dot_t(A_d, W_d, out=outs[0])
+
+    def refresh(r):
+        state["A"] = rng.integers(-128, 128, (M, K), dtype=np.int8)
+        A_d.copy_(to_dev(state["A"]))
+
+    def check_first(hosts):
+        assert np.array_equal(hosts[0], oracle.dot_t(state["A"], W))
+
+    replay_and_compare(call, [torch.empty((M, N), dtype=torch.int32, device=DEV)], refresh, check_first)
+
+
+def test_dense_dot_t_f32_replay():
+    M, K, N = 200, 128, 300
+    A, B = workloads.dense_inputs(M, K, N, 506, True)
+    A_d, B_d = to_dev(A), to_dev(B)
+    alpha = 1.0 / np.sqrt(K)
+    print("[graph] q8_dot_t_f32 M=200 K=128 N=300", flush=True)
+    rng = np.random.default_rng(507)
+    state = {"A": A}
+
+    def call(outs):
+        binding.q8_dot_t_f32(A_d, B_d, out=outs[0], alpha=alpha)
+
+    def refresh(r):
+        state["A"] = rng.standard_normal((M, K)).astype(np.float32)
+        A_d.copy_(to_dev(state["A"]))
+
+    def check_first(hosts):
+        ref = oracle.dense_fused(state["A"], B, True, alpha)
+        D = oracle.dense_fused_normaliser(state["A"], B, True, alpha)
+        err = oracle.normalised_error(hosts[0], ref, D)
+        assert err <= TOL, f"normalised error {err:.3e}"
+
+    replay_and_compare(call, [torch.empty((M, N), dtype=torch.float32, device=DEV)], refresh, check_first)
