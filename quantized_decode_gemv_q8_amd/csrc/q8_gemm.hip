@@ -360,40 +360,48 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   __syncthreads();
   if (!last_flag) return;
   // Sum the splits in K order: pairwise over groups of eight, then the groups
-  // in order (the same tree as the matvec's combine).  Thread tid owns pieces
-  // tid + 256 i, two at a time, with every load of a batch in flight.
+  // in order (the same tree as the matvec's combine).  Thread (wave, lane)
+  // sums the pieces of its own accumulator tiles, kBatch at a time with every
+  // load of a batch in flight: its own split is still in its registers, and
+  // only the other splits are read back.  A descriptor without records stands
+  // in for its own split and for the empty places of the last group of eight;
+  // its loads return zeros without a memory access.
+  const __amdgpu_buffer_rsrc_t none_rs = rsrc(p.partial, 0u);
+  constexpr int kOwn = kWaveTiles * RT;  // pieces per thread
   constexpr int kBatch = 2;
-  for (int i0 = 0; i0 < kPieces / kGThreads; i0 += kBatch) {
+  static_assert(kOwn % kBatch == 0, "whole batches of pieces");
+#pragma unroll
+  for (int j0 = 0; j0 < kOwn; j0 += kBatch) {
     f4 total[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) total[i] = f4{0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < p.splits; c += 8) {
       f4 v[kBatch][8];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i)
+      for (int i = 0; i < kBatch; ++i) {
+        const int t = (j0 + i) / RT, r = (j0 + i) % RT;
+        const uint32_t piece = (uint32_t)(((wave * kWaveTiles + t) * RT + r) * 64 + lane);
 #pragma unroll
         for (int sp = 0; sp < 8; ++sp) {
-          const uint32_t off = ((uint32_t)min(c + sp, p.splits - 1) * kPieces + tid + kGThreads * (i0 + i)) * 16u;
-          const f4 x = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(part_rs, off, 0u, kCoherent));
-          v[i][sp] = c + sp < p.splits ? x : f4{0.f, 0.f, 0.f, 0.f};
+          const int sj = c + sp;
+          const bool remote = sj < p.splits && sj != split;
+          const uint32_t off = ((uint32_t)min(sj, p.splits - 1) * kPieces + piece) * 16u;
+          const f4 x = __builtin_bit_cast(
+              f4, __builtin_amdgcn_raw_buffer_load_b128(remote ? part_rs : none_rs, off, 0u, kCoherent));
+          v[i][sp] = sj == split ? acc[t][r] : x;
         }
+      }
 #pragma unroll
       for (int i = 0; i < kBatch; ++i)
         total[i] += ((v[i][0] + v[i][1]) + (v[i][2] + v[i][3])) + ((v[i][4] + v[i][5]) + (v[i][6] + v[i][7]));
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      // Piece -> (wave, tile, row tile, lane) -> four outputs in one column.
-      const int pc = tid + kGThreads * (i0 + i);
-      const int w = pc / (kWaveTiles * RT * 64);
-      const int rem = pc - w * (kWaveTiles * RT * 64);
-      const int t = rem / (RT * 64);
-      const int r = (rem / 64) % RT;
-      const int l = rem % 64;
-      const int col = kWaveCols * w + 64 * (t >> 2) + 4 * (l & 15) + (t & 3);
+      const int t = (j0 + i) / RT, r = (j0 + i) % RT;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = 16 * r + 4 * (l >> 4) + e;
+        int m, col;
+        out_index(t, r, e, m, col);
         if (m < p.M && n0 + col < p.N) p.C[(size_t)m * p.N + n0 + col] = total[i][e];
       }
     }
