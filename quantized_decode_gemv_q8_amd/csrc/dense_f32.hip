@@ -224,16 +224,21 @@ __global__ __launch_bounds__(kThreads) void dense_split_kernel(DenseArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int tiles_m = (p.M + kTM - 1) / kTM, tiles_n = (p.N + kTN - 1) / kTN;
-  int tm, tn;
-  tile_of(blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, &tm, &tn);
-  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int tiles = tiles_m * tiles_n;
 
   const __amdgpu_buffer_rsrc_t a_rs = rsrc(p.A, (uint32_t)p.M * (uint32_t)p.K * 4u);
   const __amdgpu_buffer_rsrc_t b_rs = rsrc(p.B, (uint32_t)p.N * (uint32_t)p.K * 4u);
   const int np = (p.K + kTK - 1) / kTK;
 
-  const uint32_t a_voff = rows_voff<VEC>(tid, m0, p.K);
-  const uint32_t b_voff = TRANS_B ? rows_voff<VEC>(tid, n0, p.K) : cols_voff(tid, n0, p.N);
+  // The workgroup takes tiles v = blockIdx.x + i * gridDim.x in turn (with
+  // the grid a multiple of eight, all of them in its XCD's range).  The first
+  // panel of the next tile is loaded while the last panel of the current one
+  // is multiplied, so its latency overlaps that multiply and the stores.
+  int v = blockIdx.x;
+  int tm, tn;
+  tile_of(v, tiles, tiles_m, tiles_n, &tm, &tn);
+  uint32_t a_voff = rows_voff<VEC>(tid, tm * kTM, p.K);
+  uint32_t b_voff = TRANS_B ? rows_voff<VEC>(tid, tn * kTN, p.K) : cols_voff(tid, tn * kTN, p.N);
   auto load = [&](Panel &pa, Panel &pb, int kt) {
     sload_rows<VEC>(pa, a_rs, a_voff, p.K, kt);
     if constexpr (TRANS_B) {
@@ -252,83 +257,100 @@ __global__ __launch_bounds__(kThreads) void dense_split_kernel(DenseArgs p) {
     }
   };
 
-  f4 acc[4][4];
-  SFor<0, 4>::run([&](auto i) { SFor<0, 4>::run([&](auto j) { acc[i][j] = f4{0.f, 0.f, 0.f, 0.f}; }); });
-
   Panel pa, pb;
   load(pa, pb, 0);
-  for (int pnl = 0; pnl < np; ++pnl) {
-    const int kt = pnl * kTK;
-    if (pnl > 0) lds_barrier();  // every wave has finished reading the previous panel
-    if (p.K - kt >= kTK) {
-      stage(std::false_type{}, pa, pb, kTK);
-    } else {
-      stage(std::true_type{}, pa, pb, p.K - kt);
-    }
-    lds_barrier();
-    if (pnl + 1 < np) load(pa, pb, kt + kTK);
+  for (bool first = true;; first = false) {
+    const int m0 = tm * kTM, n0 = tn * kTN;
+    const int v_next = v + (int)gridDim.x;
+    const bool more = v_next < tiles;
+    f4 acc[4][4];
+    SFor<0, 4>::run([&](auto i) { SFor<0, 4>::run([&](auto j) { acc[i][j] = f4{0.f, 0.f, 0.f, 0.f}; }); });
 
-    // Lane l of MFMA tile (i, j) supplies row / column 16 i + l % 16 and
-    // k = 8 (l / 16) .. +7 of each part.
-    bf16x8 af[4][3], bf[4][3];
-    SFor<0, 4>::run([&](auto i) {
-      SFor<0, 3>::run([&](auto pp) {
-        af[i][pp] = *reinterpret_cast<const bf16x8 *>(a_lds + pp * kPartTile + (64 * wm + 16 * i + c16) * kSP + 8 * g4);
-        bf[i][pp] = *reinterpret_cast<const bf16x8 *>(b_lds + pp * kPartTile + (64 * wn + 16 * i + c16) * kSP + 8 * g4);
+    for (int pnl = 0; pnl < np; ++pnl) {
+      const int kt = pnl * kTK;
+      if (pnl > 0 || !first) lds_barrier();  // every wave has finished reading the previous panel
+      if (p.K - kt >= kTK) {
+        stage(std::false_type{}, pa, pb, kTK);
+      } else {
+        stage(std::true_type{}, pa, pb, p.K - kt);
+      }
+      lds_barrier();
+      if (pnl + 1 < np) {
+        load(pa, pb, kt + kTK);
+      } else if (more) {
+        tile_of(v_next, tiles, tiles_m, tiles_n, &tm, &tn);
+        a_voff = rows_voff<VEC>(tid, tm * kTM, p.K);
+        b_voff = TRANS_B ? rows_voff<VEC>(tid, tn * kTN, p.K) : cols_voff(tid, tn * kTN, p.N);
+        load(pa, pb, 0);
+      }
+
+      // Lane l of MFMA tile (i, j) supplies row / column 16 i + l % 16 and
+      // k = 8 (l / 16) .. +7 of each part.
+      bf16x8 af[4][3], bf[4][3];
+      SFor<0, 4>::run([&](auto i) {
+        SFor<0, 3>::run([&](auto pp) {
+          af[i][pp] = *reinterpret_cast<const bf16x8 *>(a_lds + pp * kPartTile + (64 * wm + 16 * i + c16) * kSP + 8 * g4);
+          bf[i][pp] = *reinterpret_cast<const bf16x8 *>(b_lds + pp * kPartTile + (64 * wn + 16 * i + c16) * kSP + 8 * g4);
+        });
       });
-    });
-    // Part products with p + q <= 2, smallest first, at raised wave priority
-    // so that the other workgroup's staging fills the gaps rather than delays them.
-    __builtin_amdgcn_s_setprio(1);
-    SFor<0, 6>::run([&](auto t) {
-      constexpr int kP[6] = {2, 1, 0, 1, 0, 0};
-      constexpr int kQ[6] = {0, 1, 2, 0, 1, 0};
+      // Part products with p + q <= 2, smallest first, at raised wave priority
+      // so that the other workgroup's staging fills the gaps rather than delays them.
+      __builtin_amdgcn_s_setprio(1);
+      SFor<0, 6>::run([&](auto t) {
+        constexpr int kP[6] = {2, 1, 0, 1, 0, 0};
+        constexpr int kQ[6] = {0, 1, 2, 0, 1, 0};
+        SFor<0, 4>::run([&](auto i) {
+          SFor<0, 4>::run([&](auto j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kP[t]], bf[j][kQ[t]], acc[i][j], 0, 0, 0);
+          });
+        });
+      });
+      __builtin_amdgcn_s_setprio(0);
+    }
+
+    // Lane l of tile (i, j) holds rows 16 i + 4 (l / 16) + e, column 16 j + l % 16.
+    // A tile wholly inside C without row factors (both uniform over the
+    // workgroup) takes straight-line stores.
+    const bool whole = m0 + kTM <= p.M && n0 + kTN <= p.N;
+    const int m_w = m0 + 64 * wm + 4 * g4, n_w = n0 + 64 * wn + c16;
+    if (whole && p.corr == nullptr) {
+      float *base = p.C + (size_t)m_w * p.N + n_w;
       SFor<0, 4>::run([&](auto i) {
         SFor<0, 4>::run([&](auto j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][kP[t]], bf[j][kQ[t]], acc[i][j], 0, 0, 0);
+          SFor<0, 4>::run([&](auto e) {
+            base[(size_t)(16 * i + e) * p.N + 16 * j] = p.alpha * acc[i][j][(int)e];
+          });
         });
       });
-    });
-    __builtin_amdgcn_s_setprio(0);
-  }
-
-  // Lane l of tile (i, j) holds rows 16 i + 4 (l / 16) + e, column 16 j + l % 16.
-  // A tile wholly inside C without row factors (both uniform over the
-  // workgroup) takes straight-line stores.
-  const bool whole = m0 + kTM <= p.M && n0 + kTN <= p.N;
-  const int m_w = m0 + 64 * wm + 4 * g4, n_w = n0 + 64 * wn + c16;
-  if (whole && p.corr == nullptr) {
-    float *base = p.C + (size_t)m_w * p.N + n_w;
-    SFor<0, 4>::run([&](auto i) {
-      SFor<0, 4>::run([&](auto j) {
-        SFor<0, 4>::run([&](auto e) {
-          base[(size_t)(16 * i + e) * p.N + 16 * j] = p.alpha * acc[i][j][(int)e];
+    } else {
+      SFor<0, 4>::run([&](auto i) {
+        SFor<0, 4>::run([&](auto j) {
+          const int n = n_w + 16 * j;
+          SFor<0, 4>::run([&](auto e) {
+            const int m = m_w + 16 * i + e;
+            if (m < p.M && n < p.N) {
+              float *c = p.C + (size_t)m * p.N + n;
+              float y = p.alpha * acc[i][j][(int)e];
+              if (p.corr) y = fmaf(p.corr[m], *c, y);
+              *c = y;
+            }
+          });
         });
       });
-    });
-    return;
+    }
+    if (!more) break;
+    v = v_next;
   }
-  SFor<0, 4>::run([&](auto i) {
-    SFor<0, 4>::run([&](auto j) {
-      const int n = n_w + 16 * j;
-      SFor<0, 4>::run([&](auto e) {
-        const int m = m_w + 16 * i + e;
-        if (m < p.M && n < p.N) {
-          float *c = p.C + (size_t)m * p.N + n;
-          float y = p.alpha * acc[i][j][(int)e];
-          if (p.corr) y = fmaf(p.corr[m], *c, y);
-          *c = y;
-        }
-      });
-    });
-  });
 }
 
 }  // namespace
 
-hipError_t launch_dense_f32(const DenseArgs &a, bool trans_b, int vec, hipStream_t stream) {
+hipError_t launch_dense_f32(const DenseArgs &a, bool trans_b, int vec, int max_wgs, hipStream_t stream) {
+  // One workgroup per tile up to max_wgs; beyond that a grid of max_wgs
+  // (rounded down to a multiple of eight) whose workgroups take several tiles.
   const int tiles = ((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN);
-  const dim3 grid((unsigned)tiles), block(kThreads);
+  const int cap = max_wgs >= 8 ? max_wgs / 8 * 8 : 8;
+  const dim3 grid((unsigned)(tiles <= cap ? tiles : cap)), block(kThreads);
   if (vec == 4) {
     if (trans_b) {
       hipLaunchKernelGGL((dense_split_kernel<true, 4>), grid, block, 0, stream, a);

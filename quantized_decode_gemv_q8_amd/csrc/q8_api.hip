@@ -427,7 +427,9 @@ q8_status dense_impl(const float *A, const float *B, float *C, int64_t M, int64_
   a.M = (int)M;
   a.K = (int)K;
   a.N = (int)N;
-  return hip_status(q8::launch_dense_f32(a, trans_b, wide ? 4 : 1, stream));
+  // Two workgroups fit a CU; with more tiles than that, each workgroup takes
+  // several and loads the next tile's first panel during its last multiply.
+  return hip_status(q8::launch_dense_f32(a, trans_b, wide ? 4 : 1, 2 * info.cus, stream));
 }
 
 }  // namespace

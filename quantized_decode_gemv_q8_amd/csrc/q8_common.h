@@ -125,7 +125,8 @@ struct DenseArgs {
 };
 
 // vec 4: every row of A and B starts 16-byte aligned; vec 1 otherwise.
-hipError_t launch_dense_f32(const DenseArgs &args, bool trans_b, int vec, hipStream_t stream);
+// max_wgs: most workgroups to launch; more tiles than that are shared out.
+hipError_t launch_dense_f32(const DenseArgs &args, bool trans_b, int vec, int max_wgs, hipStream_t stream);
 
 // Arguments of the i8 dot_t kernels.
 struct DotArgs {

@@ -82,6 +82,20 @@ def test_dense_full_size_sampled_rows(name):
 
 
 @pytest.mark.parametrize("transposed", [False, True])
+def test_more_tiles_than_workgroups(transposed):
+    # 17 x 32 = 544 tiles of 128 x 128, more than two per CU, so workgroups take
+    # several tiles in turn; ragged M, N and K, and the epilogue with row factors
+    M, K, N = 2100, 40, 4000
+    A, B = workloads.dense_inputs(M, K, N, (412, transposed), transposed)
+    rng = np.random.default_rng(413)
+    corr = rng.standard_normal(M).astype(np.float32)
+    old = rng.standard_normal((M, N)).astype(np.float32)
+    print(f"[dense] {'dot_t' if transposed else 'dot'} M={M} K={K} N={N} with row factors", flush=True)
+    assert_parity(A, B, transposed, gpu_dense(A, B, transposed, 0.5, corr, old), 0.5, corr, old)
+    assert_parity(A, B, transposed, gpu_dense(A, B, transposed))
+
+
+@pytest.mark.parametrize("transposed", [False, True])
 def test_integer_inputs_are_exact(transposed):
     rng = np.random.default_rng(402)
     M, K, N = 200, 1000, 300
