@@ -25,7 +25,9 @@
 //   * A workgroup of four wave64s owns a 128 x 128 tile of C; wave w owns the
 //     64 x 64 quarter (w / 2, w % 2) as 4 x 4 MFMA tiles of 16 x 16 (64
 //     accumulator registers per lane).  K goes in panels of 32, one MFMA
-//     k-slice.
+//     k-slice.  With more tiles than two per CU the grid stops at two
+//     workgroups per CU and each takes several tiles in turn, loading the
+//     next tile's first panel while it multiplies the current one's last.
 //   * Each thread loads its share of the next panel (A, and B) into registers
 //     while the current one is multiplied; the panel is split as it is
 //     written to LDS, as three bf16 part tiles [row][k].  One LDS buffer
