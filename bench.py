@@ -275,7 +275,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -15,7 +15,7 @@ Page: "dot and tensor cores".
     (s = s * scale; acc = acc * corr + dot) is updated as it is written; the
     epilogue is the same y = alpha * P + corr[m] * C_old as the Q8_0 one.
 
-Readings taken where the page is silent (listed in the design doc): layouts are
+Readings taken where the page is silent: layouts are
 dense row-major; K == 0 gives a zero product; C is overwritten unless the
 epilogue's row factors read it.
 """

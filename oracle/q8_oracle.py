@@ -3,7 +3,7 @@
 Pages: "Q8_0 matvec" (sections "The tensors", "Factoring out the scale",
 "Bounds") and "dot and tensor cores" (table of built-ins, "Hardware paths").
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * M > 1: the pages show one activation row; each row of A is an independent
     matvec with the same formula.
   * K not a multiple of 32: KB = ceil(K/32) scale rows; the last one applies to
