@@ -100,6 +100,37 @@ def time_steps(launch, steps, warmup, n_copies, torch):
     return wall, t_start.elapsed_time(t_end) * 1e-3
 
 
+def time_steps_graph(launch, steps, warmup, n_copies, torch):
+    """The same pass with the timed steps submitted as one HIP graph: the
+    `steps` launches are captured once on a side stream (after eager warm-up
+    launches there, which also allocate the workspace), replayed once untimed,
+    then replayed once inside the timed region.  The warm-up launches and the
+    untimed replay together make `warmup` untimed steps when warmup >= steps.
+    Returns (wall seconds, HIP-event seconds) of the timed replay."""
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for i in range(max(warmup - steps, 1)):
+            launch(i % n_copies)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(steps):
+            launch(i % n_copies)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_start.record(side)
+        g.replay()
+        t_end.record(side)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    del g
+    return wall, t_start.elapsed_time(t_end) * 1e-3
+
+
 def time_kernels(launch, steps, n_copies, torch):
     """Per-launch pass: HIP events recorded around every launch on the launch
     stream; returns the per-launch durations in milliseconds."""
@@ -260,6 +291,8 @@ def main():
     ap.add_argument("--plan", default="", help="vec,m_tile,workgroups[,kind] override, e.g. 8,1,224 or 0,0,0,2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="submit the timed steps as one captured HIP graph instead of one call each")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="short run for rocprofv3 --pmc: a few launches, then a device copy of known size")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -403,7 +436,8 @@ def main():
                           "copy_bytes": CALIB_BYTES}), flush=True)
         return
 
-    wall, gpu_s = time_steps(launch, args.steps, args.warmup, n_copies, torch)
+    timer = time_steps_graph if args.graph else time_steps
+    wall, gpu_s = timer(launch, args.steps, args.warmup, n_copies, torch)
     per = time_kernels(launch, args.steps, n_copies, torch)
     nbytes = wl.algorithmic_bytes()
     ms_per_step = wall * 1e3 / args.steps
@@ -456,6 +490,7 @@ def main():
          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "pct_of_peak": round(100.0 * value / (F32_MFMA_PEAK_TFLOPS if dense else HBM_PEAK_GBS), 2),
         "launch_us": round(launch_s * 1e6, 3),
+        "submission": "one HIP graph of the timed steps" if args.graph else "one call per step",
         "per_launch_us": {"mean": round(float(np.mean(per)) * 1e3, 3), "median": round(float(np.median(per)) * 1e3, 3),
                       "p10": round(float(np.percentile(per, 10)) * 1e3, 3),
                       "p90": round(float(np.percentile(per, 90)) * 1e3, 3)},
