@@ -18,6 +18,11 @@ show the spread but include the event packets' own overhead.
 The default warm-up is long (400 launches, about 18 ms) because the device
 needs roughly 10 ms of sustained load before the kernel settles at its
 steady-state duration.
+
+`--graph` submits the timed steps as one captured HIP graph instead of one
+call per step; it matters only for kernels shorter than a Python call.
+`--workload` picks another workload of workloads.py (the dense ones report
+TFLOP/s against the f32 matrix peak).
 """
 
 import argparse
