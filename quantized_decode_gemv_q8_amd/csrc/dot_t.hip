@@ -32,7 +32,17 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kChunkK = 128;
 constexpr int kMfmaUnroll = 8;  // chunks per wave kept in flight (all of a wave's share at K = 4096)
 
-__device__ __forceinline__ v4i load16(const int8_t *p) { return *reinterpret_cast<const v4i *>(p); }
+// Raw buffer descriptor over `bytes` bytes: a load whose offset lies past the
+// end returns zero without touching memory, so a missing chunk needs no
+// branch (a conditional load would make the compiler wait for every load
+// already in flight before it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dot_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// An offset past every operand (extents are below 2^31 bytes).
+constexpr uint32_t kOutside = 0x80000000u;
+// Cache policy of W: non-temporal (each row is read by one workgroup, once).
+constexpr int kWPolicy = 2;
 
 template <int MT>
 __global__ __launch_bounds__(kThreads) void dot_t_mfma_kernel(DotArgs p) {
@@ -49,15 +59,16 @@ __global__ __launch_bounds__(kThreads) void dot_t_mfma_kernel(DotArgs p) {
   const int c_end = min(nchunks, c_begin + cpw);
 
   // Rows past N or M read a valid row instead; their outputs are not stored.
-  const int8_t *wrow = p.W + (size_t)min(n0 + r, p.N - 1) * p.K;
-  const int8_t *arow[MT];
+  const __amdgpu_buffer_rsrc_t w_rs = dot_rsrc(p.W, (uint32_t)p.N * (uint32_t)p.K);
+  const __amdgpu_buffer_rsrc_t a_rs = dot_rsrc(p.A, (uint32_t)p.M * (uint32_t)p.K);
+  const uint32_t wrow = (uint32_t)min(n0 + r, p.N - 1) * (uint32_t)p.K;
+  uint32_t arow[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) arow[t] = p.A + (size_t)min(m0 + 16 * t + r, p.M - 1) * p.K;
+  for (int t = 0; t < MT; ++t) arow[t] = (uint32_t)min(m0 + 16 * t + r, p.M - 1) * (uint32_t)p.K;
 
   v4i acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
-  const v4i zero = {0, 0, 0, 0};
 
   for (int c0 = c_begin; c0 < c_end; c0 += kMfmaUnroll) {
     v4i w[kMfmaUnroll][2], a[kMfmaUnroll][MT][2];
@@ -65,17 +76,20 @@ __global__ __launch_bounds__(kThreads) void dot_t_mfma_kernel(DotArgs p) {
     for (int u = 0; u < kMfmaUnroll; ++u) {
       const int k = (c0 + u) * kChunkK + 32 * g;
       const bool chunk_ok = c0 + u < c_end;
-      // K % 16 == 0 on this path: each 16-byte half is wholly inside or outside K.
+      // K % 16 == 0 on this path: each 16-byte half is wholly inside or outside
+      // K.  A half outside (or a chunk past this wave's range) reads zeros.
       const bool ok0 = chunk_ok && k + 16 <= p.K;
       const bool ok1 = chunk_ok && k + 32 <= p.K;
-      w[u][0] = ok0 ? load16(wrow + k) : zero;
-      w[u][1] = ok1 ? load16(wrow + k + 16) : zero;
+      w[u][0] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, ok0 ? wrow + k : kOutside, 0u, kWPolicy);
+      w[u][1] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, ok1 ? wrow + k + 16 : kOutside, 0u, kWPolicy);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        a[u][t][0] = ok0 ? load16(arow[t] + k) : zero;
-        a[u][t][1] = ok1 ? load16(arow[t] + k + 16) : zero;
+        a[u][t][0] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, ok0 ? arow[t] + k : kOutside, 0u, 0);
+        a[u][t][1] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, ok1 ? arow[t] + k + 16 : kOutside, 0u, 0);
       }
     }
+    // Every load of the group is issued before the first multiply waits.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kMfmaUnroll; ++u)
 #pragma unroll
@@ -110,12 +124,14 @@ __global__ __launch_bounds__(kThreads) void dot_t_mfma_kernel(DotArgs p) {
 constexpr int kDotUnroll = 4;
 
 template <int LW>
-__device__ __forceinline__ void load_words(const int8_t *p, int (&x)[LW / 4]) {
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t rs, uint32_t off, int policy_nt, int (&x)[LW / 4]) {
   if constexpr (LW == 16) {
-    const v4i v = load16(p);
+    const v4i v = policy_nt ? __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0u, kWPolicy)
+                            : __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0u, 0);
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
   } else {
-    x[0] = *reinterpret_cast<const int *>(p);
+    x[0] = policy_nt ? (int)__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0u, kWPolicy)
+                     : (int)__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0u, 0);
   }
 }
 
@@ -136,10 +152,12 @@ __global__ __launch_bounds__(kThreads) void dot_t_sdot4_kernel(DotArgs p) {
   const int c = lane & 15;
   const int n = blockIdx.x * 16 + 4 * wave + (lane >> 4);
   const int m0 = blockIdx.y * MT;
-  const int8_t *wrow = p.W + (size_t)min(n, p.N - 1) * p.K;
-  const int8_t *arow[MT];
+  const __amdgpu_buffer_rsrc_t w_rs = dot_rsrc(p.W, (uint32_t)p.N * (uint32_t)p.K);
+  const __amdgpu_buffer_rsrc_t a_rs = dot_rsrc(p.A, (uint32_t)p.M * (uint32_t)p.K);
+  const uint32_t wrow = (uint32_t)min(n, p.N - 1) * (uint32_t)p.K;
+  uint32_t arow[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) arow[t] = p.A + (size_t)min(m0 + t, p.M - 1) * p.K;
+  for (int t = 0; t < MT; ++t) arow[t] = (uint32_t)min(m0 + t, p.M - 1) * (uint32_t)p.K;
 
   int acc[MT];
 #pragma unroll
@@ -151,17 +169,12 @@ __global__ __launch_bounds__(kThreads) void dot_t_sdot4_kernel(DotArgs p) {
 #pragma unroll
     for (int u = 0; u < kDotUnroll; ++u) {
       const int k = k0 + u * kStep + LW * c;
-      const bool ok = k + LW <= p.K;  // K % LW == 0 on this path
+      const bool ok = k + LW <= p.K;  // K % LW == 0 on this path; a slice past K reads zeros
+      load_words<LW>(w_rs, ok ? wrow + (uint32_t)k : kOutside, 1, w[u]);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) w[u][j] = 0;
-      if (ok) load_words<LW>(wrow + k, w[u]);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int j = 0; j < NW; ++j) a[u][t][j] = 0;
-        if (ok) load_words<LW>(arow[t] + k, a[u][t]);
-      }
+      for (int t = 0; t < MT; ++t) load_words<LW>(a_rs, ok ? arow[t] + (uint32_t)k : kOutside, 0, a[u][t]);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kDotUnroll; ++u)
 #pragma unroll
