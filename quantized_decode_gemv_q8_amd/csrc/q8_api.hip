@@ -348,7 +348,7 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
     const int64_t passes = ceil_div(M, rows);
     const size_t part =
         g.splits > 1 ? (size_t)(passes * g.n_tiles * g.splits * rows * q8::kGemmTileCols) : 1;
-    st = get_workspace(dev, stream, part, (size_t)(passes * g.n_tiles), &ws);
+    st = get_workspace(dev, stream, part, (size_t)(passes * g.n_tiles) * q8::kCounterStride, &ws);
     if (st != Q8_OK) return st;
     g.partial = ws.partial;
     g.counters = ws.counters;
@@ -380,7 +380,7 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
   {
     Workspace ws;
     st = get_workspace(dev, stream, (size_t)(L.m_chunks * L.n_tiles * L.cmax * pl.m_tile * 64 * pl.vec),
-                       (size_t)(L.m_chunks * L.n_tiles), &ws);
+                       (size_t)(L.m_chunks * L.n_tiles) * q8::kCounterStride, &ws);
     if (st != Q8_OK) return st;
     a.partial = ws.partial;
     a.counters = ws.counters;

@@ -26,6 +26,12 @@ __host__ __device__ constexpr int padded_pitch(int cols, int elem_bytes) {
 // Weight sets sharing one activation matrix in a single launch.
 constexpr int kMaxSiblings = 4;
 
+// Words between two split-K arrival counters: one counter per 128-byte line.
+// Atomics on one line are served one after another; on a small problem every
+// workgroup arrives within a microsecond, and with the counters packed
+// together they queue up (K = N = 4096: 12.9 against 10.7 us).
+constexpr int kCounterStride = 32;
+
 // Arguments of the Q8_0 matvec kernel (one launch).  The column tiles of all
 // siblings, sibling-major, form one list of n_tiles tiles; its (tile,
 // 4-block group) units, tile-major, are dealt to the n_wg workgroups of a pass
@@ -38,7 +44,7 @@ struct GemvArgs {
   const float *corr;              // [M] epilogue row factors, or null
   float alpha;                    // epilogue scale of the product
   float *partial;                 // [m_chunks][n_tiles][cmax][m_tile * 64 * vec] partial sums
-  uint32_t *counters;             // [m_chunks * n_tiles] arrival counters, zero between calls
+  uint32_t *counters;             // [m_chunks * n_tiles] arrival counters (kCounterStride apart), zero between calls
   int M, K, N, KB;
   int tiles_per;                  // column tiles of 64 * vec columns per sibling
   int n_tiles;                    // tiles over all siblings
@@ -98,7 +104,7 @@ struct GemmArgs {
   const float *S;      // [KB, N]
   float *C;            // [M, N]
   float *partial;      // [passes][n_tiles][splits][16 * RT * 512] split partials (splits > 1)
-  uint32_t *counters;  // [passes][n_tiles] arrival counters, zero between calls
+  uint32_t *counters;  // [passes][n_tiles] arrival counters (kCounterStride apart), zero between calls
   int M, K, N, KB;
   int n_tiles, splits, bps;
 };

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
     p.C += (size_t)pass * 16 * RT * p.N;
     p.M = min(16 * RT, p.M - pass * 16 * RT);
     p.partial += (size_t)pass * p.n_tiles * p.splits * kTileElems;
-    p.counters += pass * p.n_tiles;
+    p.counters += pass * p.n_tiles * kCounterStride;
   }
   const int tile = blockIdx.x;
   const int split = blockIdx.y;
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(&p.counters[tile * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = prev == (uint32_t)(p.splits - 1);
   }
   __syncthreads();
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
       }
     }
   }
-  if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&p.counters[tile * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
       const int i0 = wg_of_unit(t * p.groups, p.upw, p.rem);
       const int i1 = wg_of_unit(t * p.groups + p.groups - 1, p.upw, p.rem);
       if (i0 != i1) {
-        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[mc * p.n_tiles + t], 1u, __ATOMIC_RELAXED,
+        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         last = prev == (uint32_t)(i1 - i0);
       }
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
       const int n = (t - sib * p.tiles_per) * TW + (o - m * TW);
       if (o < MT * TW && n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, total[jo]);
     }
-    if (tid == 0) __hip_atomic_store(&p.counters[mc * p.n_tiles + t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
