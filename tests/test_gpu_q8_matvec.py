@@ -267,6 +267,18 @@ def test_non_default_stream():
     assert_parity(A, W, S, C.cpu().numpy())
 
 
+def test_many_counters():
+    # 8 row chunks x 128 column tiles: 1024 split-K counters, each on a line of
+    # its own, far more than the smallest counter allocation
+    M, K, N = 8, 2048, 8192
+    A, W, S = rand_q8(M, K, N, 116)
+    plan = {"vec": 1, "m_tile": 1, "workgroups": 512}
+    C = gpu_q8(A, W, S, plan=plan)
+    assert_parity(A, W, S, C)
+    again = gpu_q8(A, W, S, plan=plan)  # the counters were left at zero
+    assert np.array_equal(C.view(np.uint32), again.view(np.uint32))
+
+
 def test_workspace_grows_and_release():
     small = rand_q8(1, 640, 256, 114)
     big = rand_q8(4, 8192, 8192, 115)
