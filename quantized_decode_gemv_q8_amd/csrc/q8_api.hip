@@ -129,22 +129,29 @@ bool finish_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int32_t num_cus
   if (n_wg == 0) {
     // Equal runs of units, at most one workgroup per CU (a workgroup holds
     // a whole CU's registers).  A run that straddles two tiles finishes two
-    // tiles' shares at the end (two publishes, possibly two combines), which
-    // measures about 20% slower per run on MI355X than a run aligned with the
-    // tiles; so aligned runs (count dividing the tile's groups, or whole
-    // tiles) are preferred unless unaligned ones are more than 20% shorter.
-    // Among equals the larger grid wins (more loads in flight).
+    // tiles' shares at the end (two publishes, possibly two combines).
+    // Measured on MI355X over decode shapes (K 2048..28672, N 2048..12288,
+    // 1..4 rows), aligned runs (count dividing the tile's groups, or whole
+    // tiles) beat unaligned ones that are up to 1.6 times shorter, by 3-17 %,
+    // as long as the aligned grid keeps at least half the CUs busy; below that
+    // (88 workgroups) the unaligned full grid wins.  So unaligned runs are
+    // charged 1.6 times their length, and grids under half the CUs are
+    // considered only when no larger grid fits.  Among equals the larger grid
+    // wins (more loads in flight).
     int64_t cus = (int64_t)num_cus * kTargetWgsPerCu / L.m_chunks;
     if (cus < 1) cus = 1;
     const int64_t lo = ceil_div(L.units, cap);
+    const int64_t hi = L.units < cus ? L.units : cus;
+    const int64_t half = cus / 2 < hi ? cus / 2 : hi;
+    const int64_t from = lo > half ? lo : half;
     double best = 1e30;
     n_wg = lo;
-    for (int64_t w = lo; w <= (L.units < cus ? L.units : cus); ++w) {
+    for (int64_t w = from; w <= hi; ++w) {
       const int64_t count = ceil_div(L.units, w);
       const bool aligned = L.units % w == 0 && (L.G % count == 0 || count % L.G == 0);
       int nseg = q8::max_segments((int)count, (int)L.G);
       if (nseg > 32 || q8::gemv_lds_bytes(pl->vec, pl->m_tile, (int)count, nseg) > q8::kMaxGemvLds) continue;
-      const double cost = (double)count * (aligned ? 1.0 : 1.2);
+      const double cost = (double)count * (aligned ? 1.0 : 1.6);
       if (cost <= best + 1e-9) {
         best = cost;
         n_wg = w;
