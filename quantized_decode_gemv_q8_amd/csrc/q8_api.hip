@@ -181,17 +181,24 @@ bool plan_is_valid_shape(int64_t M, int64_t K, int64_t N) {
 // (each split's partial is a whole 16*ceil(M/16) x 512 tile, read back by the
 // combine), and at most 64 blocks per split (the sequential sum over a
 // split's blocks stays short).
+// K splits of an automatic matrix-core plan.
+int64_t gemm_auto_splits(int64_t M, int64_t K, int64_t N, int32_t num_cus) {
+  const int64_t n_tiles = ceil_div(N, q8::kGemmTileCols);
+  const int64_t KB = ceil_div(K, kBlock);
+  int64_t splits = (M <= 16 ? 2 : 1) * (int64_t)num_cus / n_tiles;
+  if (splits > 8) splits = 8;
+  if (splits < ceil_div(KB, 64)) splits = ceil_div(KB, 64);
+  if (splits < 1) splits = 1;
+  if (splits > KB) splits = KB;
+  return ceil_div(KB, ceil_div(KB, splits));  // no empty split
+}
+
 bool finish_gemm_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan *pl) {
   const int64_t n_tiles = ceil_div(N, q8::kGemmTileCols);
   const int64_t KB = ceil_div(K, kBlock);
   int64_t splits;
   if (pl->workgroups == 0) {
-    splits = (M <= 16 ? 2 : 1) * (int64_t)num_cus / n_tiles;
-    if (splits > 8) splits = 8;
-    if (splits < ceil_div(KB, 64)) splits = ceil_div(KB, 64);
-    if (splits < 1) splits = 1;
-    if (splits > KB) splits = KB;
-    splits = ceil_div(KB, ceil_div(KB, splits));  // no empty split
+    splits = gemm_auto_splits(M, K, N, num_cus);
   } else {
     if (pl->workgroups % n_tiles != 0) return false;
     splits = pl->workgroups / n_tiles;
@@ -212,14 +219,20 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   if (pl.kind != 0 && pl.kind != Q8_PLAN_STREAM && pl.kind != Q8_PLAN_MATRIX) return Q8_ERR_INVALID;
   const bool matrix_fits = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 && N % 16 == 0 &&
                            w_align % 16 == 0 && s_align % 16 == 0;
-  // Automatic choice.  The matrix-core product has a floor of about 16 us (its
-  // split combine), so for up to 4 rows of a small weight matrix the per-row
-  // stream is faster (K = N = 4096: 12.0 / 14.6 us at 2 / 4 rows against 17.5
-  // / 17.8); from 5 rows, or once W is large, the matrix cores win (K = N =
-  // 4096, 8 rows: 18.2 against 26.3 us; K = 8192, N = 28672, 2 rows: 50.2
-  // against 56.9 us).
-  constexpr int64_t kMatrixSmallRowsMinWeights = (int64_t)1 << 26;
-  const bool matrix_pays = M >= 5 || K * N >= kMatrixSmallRowsMinWeights;
+  // Automatic choice, from timings on MI355X under graph submission.  The
+  // per-row stream costs a multiply-add per weight and row; the matrix cores
+  // cost a split combine (a floor of about 17 us) and, with few 512-column
+  // tiles, run on few workgroups.
+  //   * From 5 rows the matrix cores win (K = N = 4096: 17.5 against 24.5 us).
+  //   * At 3-4 rows they win once K*N >= 2^25 and the product fills at least
+  //     half the CUs (K = 4096, N = 14336: 21.2 against 32.7 us), not on a
+  //     narrow W (K = 14336, N = 4096, 64 workgroups: 44.3 against 35.1).
+  //   * At 2 rows they win only from K*N >= 2^27 (K = 8192, N = 28672: 50.0
+  //     against 55.9 us; K = N = 8192: 28.4 against 21.7).
+  const bool gemm_fills = K > 0 && N > 0 &&
+      2 * ceil_div(N, q8::kGemmTileCols) * gemm_auto_splits(M, K, N, num_cus) >= (int64_t)num_cus;
+  const bool matrix_pays = M >= 5 || (M >= 3 && K * N >= ((int64_t)1 << 25) && gemm_fills) ||
+                           (M == 2 && K * N >= ((int64_t)1 << 27) && gemm_fills);
   if (pl.kind == 0)
     pl.kind = (matrix_fits && matrix_pays && M >= Q8_MATRIX_MIN_ROWS && pl.vec == 0 && pl.m_tile == 0 &&
                pl.workgroups == 0)

@@ -100,6 +100,10 @@ def test_plan_kind_follows_rows_and_layout():
     assert plan(2, 4096, 4096)["kind"] == binding.PLAN_STREAM
     assert plan(5, 4096, 4096)["kind"] == binding.PLAN_MATRIX
     assert plan(3, 8192, 28672)["kind"] == binding.PLAN_MATRIX
+    assert plan(4, 4096, 14336)["kind"] == binding.PLAN_MATRIX    # 3-4 rows: K*N >= 2^25, 224 workgroups
+    assert plan(4, 14336, 4096)["kind"] == binding.PLAN_STREAM    # a narrow W: 64 workgroups only
+    assert plan(2, 8192, 8192)["kind"] == binding.PLAN_STREAM     # 2 rows need K*N >= 2^27
+    assert plan(5, 14336, 4096)["kind"] == binding.PLAN_MATRIX
     assert plan(16, 8192, 28672)["workgroups"] == 56 * 8          # two workgroups per CU up to 16 rows
     assert plan(32, 8192, 28672)["workgroups"] == 56 * 4          # one above
     assert plan(64, 8192, 28672)["workgroups"] == 56 * 4          # one workgroup per CU
