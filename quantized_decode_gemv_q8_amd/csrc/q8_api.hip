@@ -181,12 +181,22 @@ bool plan_is_valid_shape(int64_t M, int64_t K, int64_t N) {
 // (each split's partial is a whole 16*ceil(M/16) x 512 tile, read back by the
 // combine), and at most 64 blocks per split (the sequential sum over a
 // split's blocks stays short).
-// K splits of an automatic matrix-core plan.
+// K splits of an automatic matrix-core plan: two workgroups per CU up to 16
+// rows and one above, at most 8 splits while the tiles alone nearly fill the
+// device, up to one workgroup per CU when they do not (a narrow W), never
+// under 8 or over 64 blocks per split.  Measured at 8-16 rows: K = 14336,
+// N = 4096 (8 tiles) takes 44.6 us at 8 splits and 25.9 us at 32; K = N =
+// 8192 (16 tiles) 28.8 us at 8 and 23.0 at 16; K = N = 4096 15.7 us at 16
+// splits against 17.9 at 8 and 18.8 at 32 (4 blocks each); two per CU
+// there (64 splits at 8 tiles) costs 37.5 us.
 int64_t gemm_auto_splits(int64_t M, int64_t K, int64_t N, int32_t num_cus) {
   const int64_t n_tiles = ceil_div(N, q8::kGemmTileCols);
   const int64_t KB = ceil_div(K, kBlock);
   int64_t splits = (M <= 16 ? 2 : 1) * (int64_t)num_cus / n_tiles;
-  if (splits > 8) splits = 8;
+  const int64_t one_per_cu = (int64_t)num_cus / n_tiles;
+  const int64_t cap = one_per_cu > 8 ? one_per_cu : 8;
+  if (splits > cap) splits = cap;
+  if (splits > KB / 8) splits = KB / 8;
   if (splits < ceil_div(KB, 64)) splits = ceil_div(KB, 64);
   if (splits < 1) splits = 1;
   if (splits > KB) splits = KB;
@@ -231,7 +241,11 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   //     against 55.9 us; K = N = 8192: 28.4 against 21.7).
   const bool gemm_fills = K > 0 && N > 0 &&
       2 * ceil_div(N, q8::kGemmTileCols) * gemm_auto_splits(M, K, N, num_cus) >= (int64_t)num_cus;
-  const bool matrix_pays = M >= 5 || (M >= 3 && K * N >= ((int64_t)1 << 25) && gemm_fills) ||
+  //   * Up to 16 rows (one or two passes of the stream), a W too narrow to
+  //     fill half the device stays on the stream (K = 4096, N = 1024, 16
+  //     rows: 13.4 against 15.9 us).
+  const bool matrix_pays = (M > 16) || (M >= 5 && gemm_fills) ||
+                           (M >= 3 && K * N >= ((int64_t)1 << 25) && gemm_fills) ||
                            (M == 2 && K * N >= ((int64_t)1 << 27) && gemm_fills);
   if (pl.kind == 0)
     pl.kind = (matrix_fits && matrix_pays && M >= Q8_MATRIX_MIN_ROWS && pl.vec == 0 && pl.m_tile == 0 &&

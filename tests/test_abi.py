@@ -101,7 +101,11 @@ def test_plan_kind_follows_rows_and_layout():
     assert plan(5, 4096, 4096)["kind"] == binding.PLAN_MATRIX
     assert plan(3, 8192, 28672)["kind"] == binding.PLAN_MATRIX
     assert plan(4, 4096, 14336)["kind"] == binding.PLAN_MATRIX    # 3-4 rows: K*N >= 2^25, 224 workgroups
-    assert plan(4, 14336, 4096)["kind"] == binding.PLAN_STREAM    # a narrow W: 64 workgroups only
+    assert plan(4, 14336, 4096)["kind"] == binding.PLAN_MATRIX    # a narrow W takes more splits: 8 x 32
+    assert plan(8, 14336, 4096)["workgroups"] == 8 * 32            # one workgroup per CU
+    assert plan(8, 4096, 4096)["workgroups"] == 8 * 16             # splits of at least 8 blocks
+    assert plan(16, 4096, 1024)["kind"] == binding.PLAN_STREAM     # too narrow to fill half the device
+    assert plan(64, 4096, 1024)["kind"] == binding.PLAN_MATRIX     # above 16 rows the stream needs many passes
     assert plan(2, 8192, 8192)["kind"] == binding.PLAN_STREAM     # 2 rows need K*N >= 2^27
     assert plan(5, 14336, 4096)["kind"] == binding.PLAN_MATRIX
     assert plan(16, 8192, 28672)["workgroups"] == 56 * 8          # two workgroups per CU up to 16 rows
