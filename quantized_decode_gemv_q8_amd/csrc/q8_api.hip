@@ -266,10 +266,14 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
     // 8-byte lanes (512-column tiles) measure best on MI355X for the large
     // decode shapes; 16 is used only when asked for.  Instances with
     // vec * m_tile above 16 spill registers, so they are not chosen.  A
-    // problem too small to give every CU two units at vec 8 streams for only
-    // a few microseconds and is dominated by its combine, which 4-byte lanes
-    // (twice the tiles, half the workgroups per tile) shorten: 11.0 against
-    // 12.9 us at M=1, K=N=4096.
+    // problem with fewer than three units per CU at vec 8 (few tiles or a
+    // short K) streams for only a few microseconds per workgroup and is
+    // dominated by its combine, which 4-byte lanes (twice the tiles, half the
+    // workgroups per tile) shorten.  Timed under graph submission at 1-2
+    // rows: K = N = 4096 9.1 against 10.8 us; K = 11008, N = 4096 16.1
+    // against 17.7 (19.4 against 23.9 at 2 rows); from three units per CU
+    // (K = 8192, N = 6144; K = 13824, N = 4096) vec 8 is as fast or 3-6 %
+    // faster.
     for (int v = 8; v >= 1; v >>= 1) {
       if (v * pl.m_tile <= 16 && vec_fits(v, N, w_align, s_align)) {
         pl.vec = v;
@@ -279,7 +283,7 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
     if (pl.vec == 0) return Q8_ERR_INVALID;
     if (pl.vec == 8 && vec_fits(4, N, w_align, s_align) && K > 0) {
       const int64_t units8 = n_sib * ceil_div(N, 64 * 8) * ceil_div(ceil_div(K, kBlock), q8::kWaves);
-      if (units8 < 2 * (int64_t)num_cus) pl.vec = 4;
+      if (units8 < 3 * (int64_t)num_cus) pl.vec = 4;
     }
   }
   if (pl.vec != 16 && pl.vec != 8 && pl.vec != 4 && pl.vec != 2 && pl.vec != 1) return Q8_ERR_INVALID;
