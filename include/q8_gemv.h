@@ -73,10 +73,11 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
 /*
  * Launch plan of q8_matvec.  Every field 0 means "choose automatically".
  *   kind    Q8_PLAN_STREAM or Q8_PLAN_MATRIX (below); 0 picks one from the
- *           shape: the matrix cores, when allowed, above 16 rows; at 5..16
- *           rows when their automatic plan fills at least half the device;
- *           at 3-4 rows when it does and K * N reaches 2^25; at 2 rows when
- *           it does and K * N reaches 2^27.
+ *           shape: the matrix cores, when allowed, above 16 rows; at 9..16
+ *           rows when their automatic plan fills at least a quarter of the
+ *           device, at 5..8 rows three eighths; at 3-4 rows when it fills
+ *           half and K * N reaches 2^25; at 2 rows when it fills half and
+ *           K * N reaches 2^27.
  * For Q8_PLAN_STREAM, the per-row FMA stream:
  *   vec     columns (= bytes of W) each lane loads per row: 16, 8, 4, 2 or 1.
  *           N must be a multiple of vec, W 'vec'-byte aligned and S

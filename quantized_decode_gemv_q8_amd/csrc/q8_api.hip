@@ -239,12 +239,19 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   //     narrow W (K = 14336, N = 4096, 64 workgroups: 44.3 against 35.1).
   //   * At 2 rows they win only from K*N >= 2^27 (K = 8192, N = 28672: 50.0
   //     against 55.9 us; K = N = 8192: 28.4 against 21.7).
-  const bool gemm_fills = K > 0 && N > 0 &&
-      2 * ceil_div(N, q8::kGemmTileCols) * gemm_auto_splits(M, K, N, num_cus) >= (int64_t)num_cus;
-  //   * Up to 16 rows (one or two passes of the stream), a W too narrow to
-  //     fill half the device stays on the stream (K = 4096, N = 1024, 16
-  //     rows: 13.4 against 15.9 us).
-  const bool matrix_pays = (M > 16) || (M >= 5 && gemm_fills) ||
+  const int64_t gemm_wgs =
+      K > 0 && N > 0 ? ceil_div(N, q8::kGemmTileCols) * gemm_auto_splits(M, K, N, num_cus) : 0;
+  const bool gemm_fills = 2 * gemm_wgs >= (int64_t)num_cus;     // half the CUs
+  const bool gemm_3_8ths = 8 * gemm_wgs >= 3 * (int64_t)num_cus;  // three eighths
+  const bool gemm_quarter = 4 * gemm_wgs >= (int64_t)num_cus;   // a quarter
+  //   * At 9-16 rows (two passes of the stream) the matrix cores win once
+  //     their plan fills a quarter of the CUs (K = 8192, N = 1024, 64
+  //     workgroups, 16 rows: 21.3 against 28.3 us), not below (K = 4096,
+  //     N = 1024, 32 workgroups: 15.8 against 13.5).
+  //   * At 5-8 rows (one pass) they need three eighths: K = 8192, N = 2048,
+  //     128 workgroups, 8 rows: 21.7 against 28.3 us; K = 8192, N = 1024,
+  //     64 workgroups: 20.5 against 15.4; K = 14336, N = 1024, 112: a tie.
+  const bool matrix_pays = (M > 16) || (M >= 9 && gemm_quarter) || (M >= 5 && gemm_3_8ths) ||
                            (M >= 3 && K * N >= ((int64_t)1 << 25) && gemm_fills) ||
                            (M == 2 && K * N >= ((int64_t)1 << 27) && gemm_fills);
   if (pl.kind == 0)

@@ -56,6 +56,23 @@ def test_matrix_full_size_batch():
     assert_parity(A, W, S, C)
 
 
+@pytest.mark.parametrize("M,K,N,kind,wgs", [
+    (8, 14336, 4096, binding.PLAN_MATRIX, 8 * 32),   # a narrow W: 32 splits, one workgroup per CU
+    (4, 14336, 4096, binding.PLAN_MATRIX, 8 * 32),   # 4 rows take the matrix cores there
+    (8, 4100, 4096, binding.PLAN_MATRIX, 8 * 15),    # splits of at least 8 blocks (129 blocks: 15 splits of 9, the last 3)
+    (16, 4096, 1024, binding.PLAN_STREAM, None),     # too narrow to fill half the device: the stream
+    (2, 8192, 8192, binding.PLAN_STREAM, None),      # 2 rows below K*N = 2^27: the stream
+])
+def test_automatic_plans_on_narrow_weights(M, K, N, kind, wgs):
+    plan = binding.q8_matvec_choose_plan(M, K, N)
+    assert plan["kind"] == kind
+    if wgs is not None:
+        assert plan["workgroups"] == wgs
+    A, W, S = workloads.q8_inputs(M, K, N, (320, M, K, N))
+    print(f"[gemm] automatic plan M={M} K={K} N={N}: {plan}", flush=True)
+    assert_parity(A, W, S, gpu_q8(A, W, S))
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 40])
 def test_matrix_every_split(splits):
     M, K, N = 20, 1280, 1536  # KB = 40, three tiles
