@@ -239,6 +239,7 @@ def cpu_baseline_dense(wl, A, B, alpha, rows=512, budget_s=12.0):
 
 
 CALIB_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+CALIB_COPIES = 5         # calibration copies at the end of a --pmc-pass run
 
 
 def ingest_pmc(fetch_csv, write_csv, workload, kernel_path):
@@ -248,28 +249,33 @@ def ingest_pmc(fetch_csv, write_csv, workload, kernel_path):
     import csv
 
     def per_kernel(path, counter):
-        sums, counts = {}, {}
+        """Counter value per dispatch (summed over its instances), grouped by
+        kernel name in dispatch order."""
+        sums = {}
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row.get("Counter_Name") != counter:
                     continue
-                key = (row["Kernel_Name"], row["Dispatch_Id"])
+                key = (row["Kernel_Name"], int(row["Dispatch_Id"]))
                 sums[key] = sums.get(key, 0.0) + float(row["Counter_Value"])
         by_name = {}
-        for (name, _), v in sums.items():
+        for (name, did), v in sorted(sums.items(), key=lambda kv: kv[0][1]):
             by_name.setdefault(name, []).append(v)
-        return {k: float(np.mean(v)) for k, v in by_name.items()}
+        return by_name
 
-    def pick(d, sub):
+    def pick(d, sub, last=None):
         hits = [v for k, v in d.items() if sub in k]
         if not hits:
             raise SystemExit(f"no kernel matching {sub!r} in {sorted(d)}")
-        return hits[0]
+        vals = hits[0] if last is None else hits[0][-last:]
+        return float(np.mean(vals))
 
     kname = KERNEL_NAMES[kernel_path]
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     f_k, w_k = pick(fetch, kname), pick(write, kname)
-    f_c, w_c = pick(fetch, "copyBuffer"), pick(write, "copyBuffer")
+    # The calibration copies are the pass's last CALIB_COPIES copy dispatches
+    # (earlier ones, if any, upload inputs).
+    f_c, w_c = pick(fetch, "copyBuffer", CALIB_COPIES), pick(write, "copyBuffer", CALIB_COPIES)
     ff, fw = CALIB_BYTES / (f_c * 1024.0), CALIB_BYTES / (w_c * 1024.0)
     rec = {"kernel_sha": source_hash(kernel_path), "fetch_kib": f_k, "write_kib": w_k,
            "copy_fetch_kib": f_c, "copy_write_kib": w_c, "copy_bytes": CALIB_BYTES,
@@ -434,10 +440,10 @@ def main():
             launch(i % n_copies)
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(5):
+        for _ in range(CALIB_COPIES):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"pmc_pass": wl.name, "launches": args.warmup + args.steps, "copies": 5,
+        print(json.dumps({"pmc_pass": wl.name, "launches": args.warmup + args.steps, "copies": CALIB_COPIES,
                           "copy_bytes": CALIB_BYTES}), flush=True)
         return
 
