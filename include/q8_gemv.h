@@ -92,8 +92,10 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
  * For Q8_PLAN_MATRIX, the matrix-core product of 2..64 rows ("dot and tensor
  * cores", "Hardware paths"; A is split into three bf16 parts so that the
  * result keeps f32 accuracy; one pass over W serves all rows): it needs
- * N % 16 == 0 and 16-byte aligned W and S, and serves q8_matvec,
- * q8_matvec_with_plan and a plain single-sibling fused call.
+ * N % 16 == 0, 16-byte aligned W and S and 4*M*K < 2^31 (A's byte offsets
+ * are 32-bit on this path; an explicit matrix plan beyond that returns
+ * Q8_ERR_TOO_LARGE, and automatic plans use the stream), and serves
+ * q8_matvec, q8_matvec_with_plan and a plain single-sibling fused call.
  *   vec, m_tile  must be 0.
  *   workgroups   tiles of 512 columns times K splits (a multiple of the tile
  *           count; every split gets at least one 32-row block), or 0.

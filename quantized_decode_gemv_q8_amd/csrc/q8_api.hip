@@ -227,13 +227,17 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
                        int32_t num_cus, bool matrix_ok, const q8_plan *req, q8_plan *out) {
   q8_plan pl = req ? *req : q8_plan{0, 0, 0, 0, 0};
   if (pl.kind != 0 && pl.kind != Q8_PLAN_STREAM && pl.kind != Q8_PLAN_MATRIX) return Q8_ERR_INVALID;
-  const bool matrix_fits = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 && N % 16 == 0 &&
-                           w_align % 16 == 0 && s_align % 16 == 0;
+  // The matrix kernel reads A through a buffer descriptor with 32-bit byte
+  // offsets, so A's bytes must stay below 2^31 on that path.
+  const bool matrix_a_fits = 4 * M * K < kIndexLimit;
+  const bool matrix_shape = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 && N % 16 == 0 &&
+                            w_align % 16 == 0 && s_align % 16 == 0;
+  const bool matrix_fits = matrix_shape && matrix_a_fits;
   // Automatic choice, from timings on MI355X under graph submission.  The
   // per-row stream costs a multiply-add per weight and row; the matrix cores
-  // cost a split combine (a floor of about 17 us) and, with few 512-column
-  // tiles, run on few workgroups.
-  //   * From 5 rows the matrix cores win (K = N = 4096: 17.5 against 24.5 us).
+  // cost a split combine and, with few 512-column tiles, run on few
+  // workgroups, so the choice depends on the rows and on how much of the
+  // device the matrix plan fills.
   //   * At 3-4 rows they win once K*N >= 2^25 and the product fills at least
   //     half the CUs (K = 4096, N = 14336: 21.2 against 32.7 us), not on a
   //     narrow W (K = 14336, N = 4096, 64 workgroups: 44.3 against 35.1).
@@ -260,6 +264,7 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
                   ? Q8_PLAN_MATRIX
                   : Q8_PLAN_STREAM;
   if (pl.kind == Q8_PLAN_MATRIX) {
+    if (matrix_shape && !matrix_a_fits) return Q8_ERR_TOO_LARGE;
     if (pl.waves != 0 && pl.waves != q8::kGemmWaves) return Q8_ERR_INVALID;
     if (!matrix_fits || pl.vec != 0 || pl.m_tile != 0 || pl.workgroups < 0) return Q8_ERR_INVALID;
     if (!finish_gemm_plan(M, K, N, num_cus, &pl)) return Q8_ERR_INVALID;

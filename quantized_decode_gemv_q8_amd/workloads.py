@@ -133,6 +133,56 @@ def dense_inputs(M, K, N, seed, transposed=False, dist="normal"):
     return A, B
 
 
+# ---------------------------------------------------------------- device draws
+# Inputs of several GiB (the cases at the library's 32-bit offset limits) are
+# drawn on the device with a seeded torch generator, in the distributions of
+# _draw; a host draw and copy of that size would dominate the test.  The tests
+# read back only the slices they check against the oracle.
+
+def device_generator(seed, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def device_draw(gen, dist, shape, device):
+    import torch
+    if dist == "normal":
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if dist == "u11":
+        return torch.empty(shape, device=device, dtype=torch.float32).uniform_(-1.0, 1.0, generator=gen)
+    if dist == "i8sym":
+        return torch.randint(-127, 128, shape, generator=gen, device=device, dtype=torch.int8)
+    if dist == "i8full":
+        return torch.randint(-128, 128, shape, generator=gen, device=device, dtype=torch.int8)
+    if dist == "scale":
+        return torch.empty(shape, device=device, dtype=torch.float32).uniform_(0.001, 0.02, generator=gen)
+    raise ValueError(dist)
+
+
+def device_q8_inputs(M, K, N, seed, device):
+    """q8_inputs' shapes and distributions, drawn on `device` (A, W, S in that order)."""
+    g = device_generator(seed, device)
+    A = device_draw(g, "normal", (M, K), device)
+    W = device_draw(g, "i8sym", (K, N), device)
+    S = device_draw(g, "scale", ((K + BLOCK - 1) // BLOCK, N), device)
+    return A, W, S
+
+
+def device_dot_t_inputs(M, K, N, seed, device):
+    """dot_t_inputs' shapes and distribution, drawn on `device` (A, W)."""
+    g = device_generator(seed, device)
+    return device_draw(g, "i8full", (M, K), device), device_draw(g, "i8full", (N, K), device)
+
+
+def device_dense_inputs(M, K, N, seed, transposed, device):
+    """dense_inputs' shapes and distribution, drawn on `device` (A, B)."""
+    g = device_generator(seed, device)
+    A = device_draw(g, "normal", (M, K), device)
+    return A, device_draw(g, "normal", (N, K) if transposed else (K, N), device)
+
+
 def make(name, copy=0):
     """Inputs of a named workload; copy j of a rotated set uses its own seed."""
     wl = WORKLOADS[name]

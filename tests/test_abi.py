@@ -112,6 +112,11 @@ def test_plan_kind_follows_rows_and_layout():
     assert plan(32, 8192, 28672)["workgroups"] == 56 * 4          # one above
     assert plan(64, 8192, 28672)["workgroups"] == 56 * 4          # one workgroup per CU
     assert plan(16, 28672, 28672)["workgroups"] == 56 * 14       # at most 64 blocks per split
+    # the matrix kernel addresses A with 32-bit byte offsets: 4*M*K must stay below 2^31
+    assert plan(64, (1 << 23) - 32, 16)["kind"] == binding.PLAN_MATRIX
+    assert plan(64, 1 << 23, 16)["kind"] == binding.PLAN_STREAM
+    assert plan(8, (1 << 26) - 32, 16)["kind"] == binding.PLAN_MATRIX
+    assert plan(8, 1 << 26, 16)["kind"] == binding.PLAN_STREAM
 
 
 def test_plan_workgroups_fill_the_device():
