@@ -23,6 +23,9 @@ q8_status hip_status(hipError_t e) {
 }
 
 constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // 32-bit signed element offsets
+// Largest second grid dimension of a launch.  Kernels that put row chunks
+// (or K splits) there are launched in slabs that stay within it.
+constexpr int64_t kMaxGridY = 65535;
 
 // Automatic plans give every CU one 4-wave workgroup with an equal share of W:
 // each wave keeps three chunks of rows in flight, which is enough to stream
@@ -161,7 +164,8 @@ bool finish_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int32_t num_cus
   if (n_wg < 1 || n_wg > L.units) return false;
   L = make_layout(M, K, N, n_sib, *pl, n_wg);
   if (L.count_max > cap) return false;
-  if (L.m_chunks * L.n_tiles * L.cmax * pl->m_tile * 64 * pl->vec >= kIndexLimit) return false;
+  const int64_t slab_chunks = L.m_chunks < kMaxGridY ? L.m_chunks : kMaxGridY;  // per launch
+  if (slab_chunks * L.n_tiles * L.cmax * pl->m_tile * 64 * pl->vec >= kIndexLimit) return false;
   const int nseg = q8::max_segments((int)L.count_max, (int)L.G);
   if (nseg > 32) return false;  // one bit per segment in the kernel's arrival mask
   if (q8::gemv_lds_bytes(pl->vec, pl->m_tile, (int)L.count_max, nseg) > q8::kMaxGemvLds) return false;
@@ -214,6 +218,7 @@ bool finish_gemm_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan 
     splits = pl->workgroups / n_tiles;
     if (splits < 1 || splits > KB || ceil_div(KB, ceil_div(KB, splits)) != splits) return false;
   }
+  if (splits > kMaxGridY) return false;  // the splits are the grid's second dimension
   const int64_t rows = 16 * q8::gemm_row_tiles(M) * ceil_div(M, 16 * q8::gemm_row_tiles(M));  // over all passes
   if (n_tiles * splits * rows * q8::kGemmTileCols >= kIndexLimit) return false;
   pl->workgroups = (int32_t)(n_tiles * splits);
@@ -230,8 +235,11 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   // The matrix kernel reads A through a buffer descriptor with 32-bit byte
   // offsets, so A's bytes must stay below 2^31 on that path.
   const bool matrix_a_fits = 4 * M * K < kIndexLimit;
+  // Automatic matrix plans split K into at most 64 blocks per split, and the
+  // splits must fit the grid.
   const bool matrix_shape = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 && N % 16 == 0 &&
-                            w_align % 16 == 0 && s_align % 16 == 0;
+                            w_align % 16 == 0 && s_align % 16 == 0 &&
+                            ceil_div(ceil_div(K, kBlock), 64) <= kMaxGridY;
   const bool matrix_fits = matrix_shape && matrix_a_fits;
   // Automatic choice, from timings on MI355X under graph submission.  The
   // per-row stream costs a multiply-add per weight and row; the matrix cores
@@ -427,17 +435,32 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
   a.rem = (int)L.rem;
   a.cmax = (int)L.cmax;
   a.pitch = q8::padded_pitch((int)L.count_max * kBlock, 4);
+  const int64_t slab_chunks = L.m_chunks < kMaxGridY ? L.m_chunks : kMaxGridY;
   {
     Workspace ws;
-    st = get_workspace(dev, stream, (size_t)(L.m_chunks * L.n_tiles * L.cmax * pl.m_tile * 64 * pl.vec),
-                       (size_t)(L.m_chunks * L.n_tiles) * q8::kCounterStride, &ws);
+    st = get_workspace(dev, stream, (size_t)(slab_chunks * L.n_tiles * L.cmax * pl.m_tile * 64 * pl.vec),
+                       (size_t)(slab_chunks * L.n_tiles) * q8::kCounterStride, &ws);
     if (st != Q8_OK) return st;
     a.partial = ws.partial;
     a.counters = ws.counters;
   }
   const size_t lds = q8::gemv_lds_bytes(pl.vec, pl.m_tile, (int)L.count_max,
                                        q8::max_segments((int)L.count_max, (int)L.G));
-  return hip_status(q8::launch_gemv(pl.vec, pl.m_tile, a, (int)L.m_chunks, lds, stream));
+  // Row chunks are the grid's second dimension: a taller A runs in slabs of
+  // at most kMaxGridY chunks, one launch each, in order on the stream (they
+  // share the workspace, whose counters every launch leaves at zero).
+  const int64_t slab_rows = slab_chunks * pl.m_tile;
+  for (int64_t r0 = 0; r0 < M; r0 += slab_rows) {
+    const int64_t rows = M - r0 < slab_rows ? M - r0 : slab_rows;
+    q8::GemvArgs b = a;
+    b.A = A + r0 * K;
+    for (int g = 0; g < n_sib; ++g) b.C[g] = sib[g].C + r0 * N;
+    b.corr = corr != nullptr ? corr + r0 : nullptr;
+    b.M = (int)rows;
+    st = hip_status(q8::launch_gemv(pl.vec, pl.m_tile, b, (int)ceil_div(rows, pl.m_tile), lds, stream));
+    if (st != Q8_OK) return st;
+  }
+  return Q8_OK;
 }
 
 q8_status matvec_impl(const float *A, const int8_t *W, const float *S, float *C, int64_t M,
@@ -528,14 +551,21 @@ q8_status q8_dot_t(const int8_t *A, const int8_t *W, int32_t *C, int64_t M, int6
   q8_status st = current_device(&dev, &info);
   if (st != Q8_OK) return st;
   if (K == 0) return hip_status(q8::launch_zero_fill(C, (size_t)(M * N), stream));
-  q8::DotArgs a;
-  a.A = A;
-  a.W = W;
-  a.C = C;
-  a.M = (int)M;
-  a.K = (int)K;
-  a.N = (int)N;
-  return hip_status(q8::launch_dot_t(a, stream));
+  // The kernels put chunks of at most 32 rows of A on the grid's second
+  // dimension: a taller A runs in slabs of rows, one launch each.
+  constexpr int64_t kSlabRows = kMaxGridY / 2 * 32;  // a multiple of 32 rows
+  for (int64_t r0 = 0; r0 < M; r0 += kSlabRows) {
+    q8::DotArgs a;
+    a.A = A + r0 * K;
+    a.W = W;
+    a.C = C + r0 * N;
+    a.M = (int)(M - r0 < kSlabRows ? M - r0 : kSlabRows);
+    a.K = (int)K;
+    a.N = (int)N;
+    st = hip_status(q8::launch_dot_t(a, stream));
+    if (st != Q8_OK) return st;
+  }
+  return Q8_OK;
 }
 
 q8_status q8_dot_f32(const float *A, const float *B, float *C, int64_t M, int64_t K, int64_t N,

@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "q8_common.h"
+#include "q8_sum.h"
 
 namespace q8 {
 namespace {
@@ -360,52 +361,63 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   __syncthreads();
   if (!last_flag) return;
   // Sum the splits in K order: pairwise over groups of eight, then the groups
-  // in order (the same tree as the matvec's combine).  Thread (wave, lane)
-  // sums the pieces of its own accumulator tiles, kBatch at a time with every
-  // load of a batch in flight: its own split is still in its registers, and
-  // only the other splits are read back.  A descriptor without records stands
-  // in for its own split and for the empty places of the last group of eight;
-  // its loads return zeros without a memory access.
+  // in order through the cascade of the matvec's combine (SumCascade).
+  // Thread (wave, lane) sums the pieces of its own accumulator tiles, BATCH
+  // at a time with every load of a batch in flight: its own split is still in
+  // its registers, and only the other splits are read back.  A descriptor
+  // without records stands in for its own split and for the empty places of
+  // the last group of eight; its loads return zeros without a memory access.
+  // Up to 64 splits (eight groups) the cascade is the plain sequential sum, so
+  // that case keeps one level and two pieces in flight; more splits take the
+  // full cascade one piece at a time, within the 16-row instance's registers.
   const __amdgpu_buffer_rsrc_t none_rs = rsrc(p.partial, 0u);
   constexpr int kOwn = kWaveTiles * RT;  // pieces per thread
-  constexpr int kBatch = 2;
-  static_assert(kOwn % kBatch == 0, "whole batches of pieces");
+  auto combine = [&](auto batch_, auto levels_) {
+    constexpr int BATCH = decltype(batch_)::value, LEVELS = decltype(levels_)::value;
+    static_assert(kOwn % BATCH == 0, "whole batches of pieces");
 #pragma unroll
-  for (int j0 = 0; j0 < kOwn; j0 += kBatch) {
-    f4 total[kBatch];
+    for (int j0 = 0; j0 < kOwn; j0 += BATCH) {
+      SumCascade<f4, BATCH, LEVELS> total;
+      for (int c = 0; c < p.splits; c += 8) {
+        f4 v[BATCH][8];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) total[i] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < p.splits; c += 8) {
-      f4 v[kBatch][8];
+        for (int i = 0; i < BATCH; ++i) {
+          const int t = (j0 + i) / RT, r = (j0 + i) % RT;
+          const uint32_t piece = (uint32_t)(((wave * kWaveTiles + t) * RT + r) * 64 + lane);
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
+          for (int sp = 0; sp < 8; ++sp) {
+            const int sj = c + sp;
+            const bool remote = sj < p.splits && sj != split;
+            const uint32_t off = ((uint32_t)min(sj, p.splits - 1) * kPieces + piece) * 16u;
+            const f4 x = __builtin_bit_cast(
+                f4, __builtin_amdgcn_raw_buffer_load_b128(remote ? part_rs : none_rs, off, 0u, kCoherent));
+            v[i][sp] = sj == split ? acc[t][r] : x;
+          }
+        }
+        f4 x[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+          x[i] = ((v[i][0] + v[i][1]) + (v[i][2] + v[i][3])) + ((v[i][4] + v[i][5]) + (v[i][6] + v[i][7]));
+        total.add(x);
+      }
+      f4 sum[BATCH];
+      total.result(sum);
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
         const int t = (j0 + i) / RT, r = (j0 + i) % RT;
-        const uint32_t piece = (uint32_t)(((wave * kWaveTiles + t) * RT + r) * 64 + lane);
 #pragma unroll
-        for (int sp = 0; sp < 8; ++sp) {
-          const int sj = c + sp;
-          const bool remote = sj < p.splits && sj != split;
-          const uint32_t off = ((uint32_t)min(sj, p.splits - 1) * kPieces + piece) * 16u;
-          const f4 x = __builtin_bit_cast(
-              f4, __builtin_amdgcn_raw_buffer_load_b128(remote ? part_rs : none_rs, off, 0u, kCoherent));
-          v[i][sp] = sj == split ? acc[t][r] : x;
+        for (int e = 0; e < 4; ++e) {
+          int m, col;
+          out_index(t, r, e, m, col);
+          if (m < p.M && n0 + col < p.N) p.C[(size_t)m * p.N + n0 + col] = sum[i][e];
         }
       }
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        total[i] += ((v[i][0] + v[i][1]) + (v[i][2] + v[i][3])) + ((v[i][4] + v[i][5]) + (v[i][6] + v[i][7]));
     }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int t = (j0 + i) / RT, r = (j0 + i) % RT;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int m, col;
-        out_index(t, r, e, m, col);
-        if (m < p.M && n0 + col < p.N) p.C[(size_t)m * p.N + n0 + col] = total[i][e];
-      }
-    }
-  }
+  };
+  if (p.splits <= 64)
+    combine(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+  else
+    combine(std::integral_constant<int, 1>{}, std::integral_constant<int, 6>{});
   if (tid == 0) __hip_atomic_store(&p.counters[tile * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "q8_common.h"
+#include "q8_sum.h"
 
 namespace q8 {
 namespace {
@@ -558,17 +559,15 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
     const int contributors = wg_of_unit(t * p.groups + p.groups - 1, p.upw, p.rem) - i0 + 1;
     // Each thread owns OPT outputs.  The summation order is the same for every
     // instance: a pairwise tree over each group of eight contributors (absent
-    // ones are zero), then the group sums in K order.  Loads come in batches
-    // of whole groups, for all of the thread's outputs at once; they are
-    // device-coherent, so they see the other workgroups' published partials
-    // without invalidating this XCD's L2.
+    // ones are zero), then the group sums in K order through a cascade
+    // (SumCascade).  Loads come in batches of whole groups, for all of the
+    // thread's outputs at once; they are device-coherent, so they see the
+    // other workgroups' published partials without invalidating this XCD's L2.
     constexpr int OPT = (MT * TW + kThreads - 1) / kThreads;
     constexpr int kGroup = 8;
     constexpr int NBT = OPT <= 2 ? 4 * kGroup : OPT == 4 ? 2 * kGroup : kGroup;
     const float *src = p.partial + (size_t)(mc * p.n_tiles + t) * p.cmax * (MT * TW);
-    float total[OPT];
-#pragma unroll
-    for (int jo = 0; jo < OPT; ++jo) total[jo] = 0.f;
+    SumCascade<float, OPT> total;
     for (int c = 0; c < contributors; c += NBT) {
       float v[OPT][NBT];
 #pragma unroll
@@ -582,20 +581,25 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
                          : 0.f;
         }
 #pragma unroll
-      for (int jo = 0; jo < OPT; ++jo)
+      for (int g = 0; g < NBT; g += kGroup) {
+        float x[OPT];
 #pragma unroll
-        for (int g = 0; g < NBT; g += kGroup) {
-          float *x = &v[jo][g];
-          total[jo] += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+        for (int jo = 0; jo < OPT; ++jo) {
+          const float *y = &v[jo][g];
+          x[jo] = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
         }
+        total.add(x);
+      }
     }
+    float sum[OPT];
+    total.result(sum);
     const int sib = t / p.tiles_per;
 #pragma unroll
     for (int jo = 0; jo < OPT; ++jo) {
       const int o = tid + kThreads * jo;
       const int m = o / TW;
       const int n = (t - sib * p.tiles_per) * TW + (o - m * TW);
-      if (o < MT * TW && n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, total[jo]);
+      if (o < MT * TW && n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, sum[jo]);
     }
     if (tid == 0) __hip_atomic_store(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

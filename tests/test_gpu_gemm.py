@@ -81,6 +81,23 @@ def test_matrix_every_split(splits):
     assert_parity(A, W, S, C)
 
 
+@pytest.mark.parametrize("M,K,N,splits", [
+    (16, 18432, 1024, 64),    # eight groups of splits: the plain sequential sum
+    (16, 18432, 1024, 72),    # nine groups: the cascade, one piece at a time
+    (40, 18432, 1024, 576),   # 72 groups of one-block splits: two cascade levels, 64-row instance
+    (16, 1 << 20, 16, None),  # automatic: 512 splits of 64 blocks
+])
+def test_matrix_many_splits(M, K, N, splits):
+    plan = {"kind": binding.PLAN_MATRIX}
+    if splits is not None:
+        plan["workgroups"] = (N // 512 or 1) * splits
+    else:
+        assert binding.q8_matvec_choose_plan(M, K, N)["workgroups"] == 512
+    A, W, S = workloads.q8_inputs(M, K, N, (330, M, K, N))
+    print(f"[gemm] M={M} K={K} N={N} splits={splits}", flush=True)
+    assert_parity(A, W, S, gpu_q8(A, W, S, plan))
+
+
 def test_matrix_and_stream_agree_with_the_oracle():
     A, W, S = workloads.q8_inputs(12, 3000, 2048, 302)
     assert_parity(A, W, S, gpu_q8(A, W, S, MATRIX))

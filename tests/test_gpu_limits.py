@@ -123,3 +123,46 @@ def test_dense_at_the_byte_limit(transposed):
     release()
     err = oracle.normalised_error(Cs, ref, D)
     assert err <= TOL, f"normalised error {err:.3e}"
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def test_tall_a_runs_in_row_slabs():
+    """600 000 rows in chunks of 8 are 75 000 row chunks, more than the grid's
+    second dimension holds (65 535): the library launches slabs of rows in
+    order.  Two siblings and row factors check that every slab offsets A,
+    each C and corr alike."""
+    M, K, N, alpha = 600_000, 64, 64, 0.75
+    assert binding.q8_matvec_choose_plan(M, K, N)["m_tile"] == 8
+    A, Ws, Ss = workloads.q8_fused_inputs(M, K, N, 2, (607, 0))
+    rng = np.random.default_rng(608)
+    corr = rng.standard_normal(M).astype(np.float32)
+    C_olds = [rng.standard_normal((M, N)).astype(np.float32) for _ in range(2)]
+    print(f"[limits] q8_matvec_fused M={M} K={K} N={N} siblings=2 with corr", flush=True)
+    outs = [to_dev(C) for C in C_olds]
+    binding.q8_matvec_fused(to_dev(A), [to_dev(W) for W in Ws], [to_dev(S) for S in Ss], outs=outs,
+                            alpha=alpha, corr=to_dev(corr))
+    torch.cuda.synchronize()
+    got = [o.cpu().numpy() for o in outs]
+    del outs
+    release()
+    refs = oracle.q8_matvec_fused(A, list(zip(Ws, Ss)), alpha, corr, C_olds)
+    for g in range(2):
+        D = oracle.q8_fused_normaliser(A, Ws[g], Ss[g], alpha, corr, C_olds[g])
+        err = oracle.normalised_error(got[g], refs[g], D)
+        assert err <= TOL, f"sibling {g}: normalised error {err:.3e}"
+
+
+@pytest.mark.parametrize("K", [16, 20])  # the i8 matrix cores; sdot4 with 16 rows per grid row
+def test_dot_t_tall_a_runs_in_row_slabs(K):
+    M, N = 1_100_000, 16
+    A, W = workloads.dot_t_inputs(M, K, N, (609, K))
+    print(f"[limits] q8_dot_t M={M} K={K} N={N}", flush=True)
+    C = binding.q8_dot_t(to_dev(A), to_dev(W))
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    del C
+    release()
+    assert np.array_equal(got, oracle.dot_t(A, W))

@@ -267,6 +267,17 @@ def test_non_default_stream():
     assert_parity(A, W, S, C.cpu().numpy())
 
 
+@pytest.mark.parametrize("M,K,N,contributors", [(1, 1 << 20, 64, 512), (3, 1 << 20, 64, 2048)])
+def test_long_k_many_contributors(M, K, N, contributors):
+    """A long K over one column tile: 512 (one row) and 2048 (three rows, four
+    units per workgroup) workgroups share the tile, so the combine sums 64
+    and 256 groups of eight partials through its cascade."""
+    plan = {"kind": binding.PLAN_STREAM}
+    A, W, S = rand_q8(M, K, N, (140, M, K, N))
+    print(f"[q8] long K M={M} K={K} N={N} stream, {contributors} contributors", flush=True)
+    assert_parity(A, W, S, gpu_q8(A, W, S, plan))
+
+
 def test_many_counters():
     # 8 row chunks x 128 column tiles: 1024 split-K counters, each on a line of
     # its own, far more than the smallest counter allocation
