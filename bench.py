@@ -55,10 +55,6 @@ KERNEL_NAMES = {KERNEL_SRC: "q8_gemv_kernel", GEMM_SRC: "q8_gemm_kernel", DOT_SR
                 DENSE_SRC: "dense_split_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
-# Rotated copies per workload: enough to exceed the Infinity Cache (>= 1 GiB).
-COPIES = {"tiny": 1, "attn4096": 57, "mlp_up_8192x28672": 4, "mlp_down_28672x8192": 4,
-          "ragged_m4": 47, "dot_t_16x4096x4096": 63, "mlp_gate_up_8192x28672": 2, "attn_qkv_4096": 19,
-          "batch16_8192x28672": 4, "batch64_8192x28672": 4, "dot_f32_4096": 1, "scores_4096x4096_d128": 1}
 
 
 def source_hash(paths):
@@ -329,7 +325,7 @@ def main():
     from quantized_decode_gemv_q8_amd import binding, workloads
 
     wl = workloads.WORKLOADS[args.workload]
-    n_copies = args.copies or COPIES.get(args.workload, 1)
+    n_copies = args.copies or workloads.COPIES.get(args.workload, 1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {wl.name} M={wl.M} K={wl.K} N={wl.N} copies={n_copies}", file=sys.stderr, flush=True)

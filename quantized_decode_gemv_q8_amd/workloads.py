@@ -79,6 +79,14 @@ WORKLOADS = {
 }
 
 
+# Rotated copies per workload: enough to exceed the 256 MB Infinity Cache
+# (at least 1 GiB of weights), so that a timed pass reads its weights from
+# HBM.  Copy j draws from its own seed (``make(name, j)``).
+COPIES = {"tiny": 1, "attn4096": 57, "mlp_up_8192x28672": 4, "mlp_down_28672x8192": 4,
+          "ragged_m4": 47, "dot_t_16x4096x4096": 63, "mlp_gate_up_8192x28672": 2, "attn_qkv_4096": 19,
+          "batch16_8192x28672": 4, "batch64_8192x28672": 4, "dot_f32_4096": 1, "scores_4096x4096_d128": 1}
+
+
 def _draw(rng, dist, shape):
     if dist == "u11":
         return rng.uniform(-1.0, 1.0, shape).astype(np.float32)

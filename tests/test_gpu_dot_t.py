@@ -23,6 +23,17 @@ def test_workload_bit_exact():
     assert np.array_equal(gpu_dot_t(A, W), oracle.dot_t(A, W))
 
 
+def test_workload_every_rotated_copy():
+    """Every rotated copy the bench streams (63), bit-exact."""
+    n = workloads.COPIES["dot_t_16x4096x4096"]
+    print(f"[dot_t] 16x4096x4096: {n} rotated copies", flush=True)
+    for j in range(1, n):
+        if j % 16 == 0:
+            print(f"[dot_t] copy {j}", flush=True)
+        A, W = workloads.make("dot_t_16x4096x4096", j)
+        assert np.array_equal(gpu_dot_t(A, W), oracle.dot_t(A, W)), f"copy {j}"
+
+
 @pytest.mark.parametrize("M", list(range(1, 18)) + [31, 32, 33, 64])
 def test_rows_mfma_and_sdot4(M):
     for K, N in [(4096, 300), (128, 17), (4100, 64), (64, 1000)]:

@@ -57,7 +57,13 @@ def test_workload_parity(name):
 
 @pytest.mark.parametrize("name", ["attn4096", "ragged_m4"])
 def test_workload_rotated_copies(name):
-    for j in (1, 2):
+    """Every rotated copy the bench streams (57 and 47), each against the oracle."""
+    n = workloads.COPIES[name]
+    assert n > 1
+    print(f"[q8] workload {name}: {n} rotated copies", flush=True)
+    for j in range(1, n):
+        if j % 16 == 0:
+            print(f"[q8] {name}: copy {j}", flush=True)
         A, W, S = workloads.make(name, j)
         assert_parity(A, W, S, gpu_q8(A, W, S))
 
