@@ -98,7 +98,8 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
  * q8_matvec, q8_matvec_with_plan and a plain single-sibling fused call.
  *   vec, m_tile  must be 0.
  *   workgroups   tiles of 512 columns times K splits (a multiple of the tile
- *           count; every split gets at least one 32-row block), or 0.
+ *           count; every split gets at least one 32-row block; at most 65535
+ *           splits), or 0.
  *   waves   8 or 0 (eight waves per workgroup, 64 columns each).
  */
 #define Q8_PLAN_STREAM 1
