@@ -95,7 +95,10 @@ def test_matrix_many_splits(M, K, N, splits):
         assert binding.q8_matvec_choose_plan(M, K, N)["workgroups"] == 512
     A, W, S = workloads.q8_inputs(M, K, N, (330, M, K, N))
     print(f"[gemm] M={M} K={K} N={N} splits={splits}", flush=True)
-    assert_parity(A, W, S, gpu_q8(A, W, S, plan))
+    C = gpu_q8(A, W, S, plan)
+    assert_parity(A, W, S, C)
+    assert np.array_equal(gpu_q8(A, W, S, plan), C)  # a fixed summation order
+    assert np.array_equal(gpu_q8(A, W, np.float32(4.0) * S, plan), np.float32(4.0) * C)
 
 
 def test_matrix_and_stream_agree_with_the_oracle():

@@ -281,7 +281,12 @@ def test_long_k_many_contributors(M, K, N, contributors):
     plan = {"kind": binding.PLAN_STREAM}
     A, W, S = rand_q8(M, K, N, (140, M, K, N))
     print(f"[q8] long K M={M} K={K} N={N} stream, {contributors} contributors", flush=True)
-    assert_parity(A, W, S, gpu_q8(A, W, S, plan))
+    C = gpu_q8(A, W, S, plan)
+    assert_parity(A, W, S, C)
+    # The cascade's order depends only on the contributor count: repeated
+    # calls agree bitwise, and scaling A by a power of two scales C exactly.
+    assert np.array_equal(gpu_q8(A, W, S, plan), C)
+    assert np.array_equal(gpu_q8(np.float32(0.25) * A, W, S, plan), np.float32(0.25) * C)
 
 
 def test_many_counters():
