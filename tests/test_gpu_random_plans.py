@@ -5,7 +5,8 @@ The fixed sweeps cover each kernel instance on chosen shapes; this one draws
 shapes and plans at random (a fixed seed per case, so every run checks the
 same cases): ragged K and N, every stream instance (vec, m_tile) with any
 workgroup count the run-length cap allows, matrix-core plans with any valid
-split count, and the i8 dot_t and dense f32 products on random extents.  A
+split count, fused siblings through the epilogue, and the i8 dot_t and dense
+f32 products on random extents.  A
 plan the library refuses up front (a run whose segments exceed the LDS
 budget) must be refused with Q8_ERR_INVALID; every other case must meet the
 oracle's bar.
@@ -106,3 +107,37 @@ def test_random_dense_shapes(transposed):
         D = oracle.dense_fused_normaliser(A, B, transposed, alpha)
         err = oracle.normalised_error(C.cpu().numpy(), ref, D)
         assert err <= TOL, f"M={M} K={K} N={N}: normalised error {err:.3e}"
+
+
+def test_random_fused_siblings():
+    """1-4 sibling weight sets sharing A, through the epilogue with random
+    alpha and (every other case) row factors, under random stream plans."""
+    ran = 0
+    for i in range(CASES // 2):
+        rng = np.random.default_rng((708, i))
+        M, K, N, plan = draw_stream_case(1000 + i)
+        n_sib = int(rng.integers(1, 5))
+        alpha = float(rng.choice([1.0, -0.5, 3.0]))
+        A, Ws, Ss = workloads.q8_fused_inputs(M, K, N, n_sib, (709, i))
+        corr = rng.standard_normal(M).astype(np.float32) if i % 2 else None
+        C_olds = [rng.standard_normal((M, N)).astype(np.float32) for _ in range(n_sib)] if i % 2 else None
+        units = n_sib * math.ceil(N / (64 * plan["vec"])) * math.ceil(math.ceil(K / 32) / 4)
+        lo = math.ceil(units / (16 // plan["m_tile"]))
+        plan["workgroups"] = int(rng.integers(lo, units + 1))  # the units of every sibling
+        print(f"[random] fused M={M} K={K} N={N} siblings={n_sib} alpha={alpha} corr={corr is not None} "
+              f"plan={plan}", flush=True)
+        outs = [to_dev(C) for C in C_olds] if C_olds else None
+        try:
+            got = binding.q8_matvec_fused(to_dev(A), [to_dev(W) for W in Ws], [to_dev(S) for S in Ss], outs=outs,
+                                          alpha=alpha, corr=to_dev(corr) if corr is not None else None, plan=plan)
+        except binding.Q8Error as e:
+            assert e.status == binding.Q8_ERR_INVALID, str(e)
+            continue
+        torch.cuda.synchronize()
+        refs = oracle.q8_matvec_fused(A, list(zip(Ws, Ss)), alpha, corr, C_olds)
+        for g in range(n_sib):
+            D = oracle.q8_fused_normaliser(A, Ws[g], Ss[g], alpha, corr, C_olds[g] if C_olds else None)
+            err = oracle.normalised_error(got[g].cpu().numpy(), refs[g], D)
+            assert err <= TOL, f"case {i} sibling {g}: normalised error {err:.3e}"
+        ran += 1
+    assert ran >= CASES // 2 * 3 // 4
