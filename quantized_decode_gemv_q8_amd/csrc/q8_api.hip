@@ -153,7 +153,7 @@ bool finish_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int32_t num_cus
       const int64_t count = ceil_div(L.units, w);
       const bool aligned = L.units % w == 0 && (L.G % count == 0 || count % L.G == 0);
       int nseg = q8::max_segments((int)count, (int)L.G);
-      if (nseg > 32 || q8::gemv_lds_bytes(pl->vec, pl->m_tile, (int)count, nseg) > q8::kMaxGemvLds) continue;
+      if (nseg > q8::kMaxSegments || q8::gemv_lds_bytes(pl->vec, pl->m_tile, (int)count, nseg) > q8::kMaxGemvLds) continue;
       const double cost = (double)count * (aligned ? 1.0 : 1.6);
       if (cost <= best + 1e-9) {
         best = cost;
@@ -167,7 +167,7 @@ bool finish_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int32_t num_cus
   const int64_t slab_chunks = L.m_chunks < kMaxGridY ? L.m_chunks : kMaxGridY;  // per launch
   if (slab_chunks * L.n_tiles * L.cmax * pl->m_tile * 64 * pl->vec >= kIndexLimit) return false;
   const int nseg = q8::max_segments((int)L.count_max, (int)L.G);
-  if (nseg > 32) return false;  // one bit per segment in the kernel's arrival mask
+  if (nseg > q8::kMaxSegments) return false;  // one arrival bit per segment in the kernel
   if (q8::gemv_lds_bytes(pl->vec, pl->m_tile, (int)L.count_max, nseg) > q8::kMaxGemvLds) return false;
   pl->workgroups = (int32_t)n_wg;
   pl->waves = q8::kWaves;

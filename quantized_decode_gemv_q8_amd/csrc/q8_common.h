@@ -90,6 +90,10 @@ inline size_t gemv_lds_bytes(int vec, int m_tile, int count, int nseg) {
   return stage + scales + slots;
 }
 
+// Most tiles one workgroup's run may touch: the epilogue keeps one arrival
+// bit and one contributor range per tile.
+constexpr int kMaxSegments = 32;
+
 // Most tiles a run of `count` (tile, group) units touches, with `groups`
 // groups per tile.
 constexpr int max_segments(int count, int groups) { return (count - 1 + groups - 1) / groups + 1; }

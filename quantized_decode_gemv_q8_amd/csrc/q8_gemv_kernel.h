@@ -422,6 +422,35 @@ __device__ __forceinline__ void store_out(const GemvArgs &p, int sib, int row, i
   *c = y;
 }
 
+// Stores outputs 4*o4 .. 4*o4+3 of row chunk m0's tile (sibling sib, tile
+// tis within the sibling), [MT][TW] in tile order, through the epilogue;
+// columns past N and rows past M are not stored.
+template <int TW>
+__device__ __forceinline__ void store_quad(const GemvArgs &p, int sib, int tis, int m0, int o4, v4f x) {
+  const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int o = 4 * o4 + e;
+    const int m = o / TW;
+    const int n = tis * TW + (o - m * TW);
+    if (n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, xs[e]);
+  }
+}
+
+// Cache policy of the split-K partials' stores and loads: device-coherent
+// (sc1), as for agent-scope atomic loads and stores.  A store is acknowledged
+// once it is performed at the device's coherence point; a load misses in the
+// per-XCD caches and reads that point.
+constexpr int kDeviceCoherent = 16;
+// Contributors summed by one pairwise tree in a split-K combine.
+constexpr int kCombineGroup = 8;
+// Outputs 4*o4 .. 4*o4+3 of contributor c's partial (stride `per` floats).
+__device__ __forceinline__ v4f load_partial_quad(__amdgpu_buffer_rsrc_t rs, int c, int o4, int per) {
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, ((uint32_t)c * (uint32_t)per + 4u * (uint32_t)o4) * 4u, 0,
+                                                      kDeviceCoherent);
+  return v4f{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+}
+
 // Workgroup that owns unit u when units are dealt in runs of upw (+1 for the
 // first rem workgroups).
 __device__ __forceinline__ int wg_of_unit(int u, int upw, int rem) {
@@ -493,6 +522,11 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
     const bool ok = m < MT && m0 + m < p.M && k < p.K;
     sv[q] = ok ? p.A[(size_t)(m0 + m) * p.K + k] : 0.f;
   }
+  // Contributors [seg_lo, seg_hi] (workgroups) of each tile the run touches,
+  // worked out by wave 0 while its first loads are in flight: the epilogue
+  // then starts without integer divisions.
+  __shared__ int seg_lo[kMaxSegments], seg_hi[kMaxSegments];
+  const int nseg = t_last - t_first + 1;
   st.run(count * CPB, [&]() {
 #pragma unroll
     for (int q = 0; q < kStageRegs; ++q) {
@@ -500,47 +534,55 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
       const int m = e / per_m;
       if (m < MT) stage[m * p.pitch + (e - m * per_m)] = sv[q];
     }
+    if (wave == 0 && lane < nseg) {
+      const int t = t_first + lane;
+      seg_lo[lane] = wg_of_unit(t * p.groups, p.upw, p.rem);
+      seg_hi[lane] = wg_of_unit(t * p.groups + p.groups - 1, p.upw, p.rem);
+    }
   });
   lds_barrier();
 
-  // Finish every tile of the run: the four waves' sums, then a direct store
-  // (the run owns the whole tile) or a published partial.
-  const int nseg = t_last - t_first + 1;
+  // Finish every tile of the run: the four waves' sums, four adjacent outputs
+  // per thread, then a direct store (the run owns the whole tile) or a
+  // published partial (one 16-byte device-coherent store per thread).
+  constexpr int kQuads = MT * TW / 4;
   bool any_partial = false;
   for (int q = 0; q < nseg; ++q) {
     const int t = t_first + q;
-    const int i0 = wg_of_unit(t * p.groups, p.upw, p.rem);
-    const int i1 = wg_of_unit(t * p.groups + p.groups - 1, p.upw, p.rem);
-    const int sib = t / p.tiles_per;
-    const float *sl = slots + (size_t)q * (kWaves * MT * TW);
-    float *mine = p.partial + ((size_t)(mc * p.n_tiles + t) * p.cmax + (wg - i0)) * (MT * TW);
+    const int i0 = seg_lo[q], i1 = seg_hi[q];
+    const v4f *sl = reinterpret_cast<const v4f *>(slots + (size_t)q * (kWaves * MT * TW));
     any_partial |= i0 != i1;
-    for (int o = tid; o < MT * TW; o += kThreads) {
-      const float x = (sl[o] + sl[MT * TW + o]) + (sl[2 * MT * TW + o] + sl[3 * MT * TW + o]);
-      const int m = o / TW;
-      const int n = (t - sib * p.tiles_per) * TW + (o - m * TW);
-      if (i0 == i1) {
-        if (n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, x);
-      } else {
-        // Device-coherent store (written through to the agent's coherence
-        // point): no whole-cache write-back is needed to publish it.
-        __hip_atomic_store(&mine[o], x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i0 == i1) {
+      const int sib = t / p.tiles_per;
+      for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
+        const v4f x = (sl[o4] + sl[kQuads + o4]) + (sl[2 * kQuads + o4] + sl[3 * kQuads + o4]);
+        store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, x);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc(p.partial + ((size_t)(mc * p.n_tiles + t) * p.cmax + (wg - i0)) * (MT * TW), MT * TW * 4);
+      for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
+        const v4f x = (sl[o4] + sl[kQuads + o4]) + (sl[2 * kQuads + o4] + sl[3 * kQuads + o4]);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v4u{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)}, rs,
+            (uint32_t)o4 * 16u, 0, kDeviceCoherent);
       }
     }
   }
   if (!any_partial) return;
 
-  // Count each shared tile's contribution once this workgroup's stores have
-  // completed: lane q of wave 0 bumps segment q's counter, all in one go.  The
-  // last of a tile's contributors combines it.
+  // Count each shared tile's contribution once this workgroup's partials are
+  // performed at device scope (s_waitcnt: the coherent stores are
+  // acknowledged only when they have reached the device's coherence point):
+  // lane q of wave 0 bumps segment q's counter, all in one go.  The last of a
+  // tile's contributors combines it.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (wave == 0) {
     bool last = false;
     if (lane < nseg) {
       const int t = t_first + lane;
-      const int i0 = wg_of_unit(t * p.groups, p.upw, p.rem);
-      const int i1 = wg_of_unit(t * p.groups + p.groups - 1, p.upw, p.rem);
+      const int i0 = seg_lo[lane], i1 = seg_hi[lane];
       if (i0 != i1) {
         const uint32_t prev = __hip_atomic_fetch_add(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
@@ -555,51 +597,39 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
   for (int q = 0; q < nseg; ++q) {
     if (!(last_mask & (1u << q))) continue;
     const int t = t_first + q;
-    const int i0 = wg_of_unit(t * p.groups, p.upw, p.rem);
-    const int contributors = wg_of_unit(t * p.groups + p.groups - 1, p.upw, p.rem) - i0 + 1;
-    // Each thread owns OPT outputs.  The summation order is the same for every
-    // instance: a pairwise tree over each group of eight contributors (absent
-    // ones are zero), then the group sums in K order through a cascade
-    // (SumCascade).  Loads come in batches of whole groups, for all of the
-    // thread's outputs at once; they are device-coherent, so they see the
-    // other workgroups' published partials without invalidating this XCD's L2.
-    constexpr int OPT = (MT * TW + kThreads - 1) / kThreads;
-    constexpr int kGroup = 8;
-    constexpr int NBT = OPT <= 2 ? 4 * kGroup : OPT == 4 ? 2 * kGroup : kGroup;
-    const float *src = p.partial + (size_t)(mc * p.n_tiles + t) * p.cmax * (MT * TW);
-    SumCascade<float, OPT> total;
-    for (int c = 0; c < contributors; c += NBT) {
-      float v[OPT][NBT];
-#pragma unroll
-      for (int i = 0; i < NBT; ++i)
-#pragma unroll
-        for (int jo = 0; jo < OPT; ++jo) {
-          const int o = min(tid + kThreads * jo, MT * TW - 1);
-          v[jo][i] = c + i < contributors
-                         ? __hip_atomic_load(&src[(size_t)(c + i) * (MT * TW) + o], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)
-                         : 0.f;
-        }
-#pragma unroll
-      for (int g = 0; g < NBT; g += kGroup) {
-        float x[OPT];
-#pragma unroll
-        for (int jo = 0; jo < OPT; ++jo) {
-          const float *y = &v[jo][g];
-          x[jo] = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
-        }
-        total.add(x);
-      }
-    }
-    float sum[OPT];
-    total.result(sum);
+    const int i0 = seg_lo[q];
+    const int contributors = seg_hi[q] - i0 + 1;
+    // Each thread owns four adjacent outputs.  The summation order is the
+    // same for every instance: a pairwise tree over each group of eight
+    // contributors (absent ones are zero), then the group sums in K order
+    // through a cascade (SumCascade).  The partials are read with 16-byte
+    // device-coherent loads, two groups per round trip; the descriptor ends
+    // at the last contributor, so reads past it return zero.
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.partial + (size_t)(mc * p.n_tiles + t) * p.cmax * (MT * TW),
+                                                  (uint32_t)contributors * (MT * TW * 4));
     const int sib = t / p.tiles_per;
+    for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
+      SumCascade<float, 4> total;
+      for (int c = 0; c < contributors; c += 2 * kCombineGroup) {
+        v4f v[2 * kCombineGroup];
 #pragma unroll
-    for (int jo = 0; jo < OPT; ++jo) {
-      const int o = tid + kThreads * jo;
-      const int m = o / TW;
-      const int n = (t - sib * p.tiles_per) * TW + (o - m * TW);
-      if (o < MT * TW && n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, sum[jo]);
+        for (int i = 0; i < kCombineGroup; ++i) v[i] = load_partial_quad(rs, c + i, o4, MT * TW);
+        const bool second = contributors - c > kCombineGroup;
+        if (second) {
+#pragma unroll
+          for (int i = kCombineGroup; i < 2 * kCombineGroup; ++i) v[i] = load_partial_quad(rs, c + i, o4, MT * TW);
+        }
+#pragma unroll
+        for (int g = 0; g < (second ? 2 : 1) * kCombineGroup; g += kCombineGroup) {
+          const v4f *y = &v[g];
+          const v4f s = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
+          const float x[4] = {s.x, s.y, s.z, s.w};
+          total.add(x);
+        }
+      }
+      float sum[4];
+      total.result(sum);
+      store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, v4f{sum[0], sum[1], sum[2], sum[3]});
     }
     if (tid == 0) __hip_atomic_store(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
