@@ -28,13 +28,17 @@
  *     library uses 32-bit element offsets, so K*N, M*K and M*N must each be
  *     below 2^31 (otherwise Q8_ERR_TOO_LARGE).
  *   - Thread safety: concurrent calls are safe on distinct streams.  Host
- *     threads that share one stream must serialise their calls: a call that
- *     needs a larger workspace frees the stream's smaller one.  The split-K
- *     workspace of q8_matvec is owned by the library, one per (device,
- *     stream); it is allocated on the first call that needs it on that
- *     stream (so that first call must not run under stream capture) and
- *     freed by q8_release().  Later calls on that stream may be captured
- *     into a HIP graph and replayed: their arrival counters return to zero
+ *     threads that share one stream must serialise their calls.
+ *   - Workspace: the split-K workspace (partial sums and arrival counters)
+ *     is owned by the library, one per (device, stream).  It is allocated by
+ *     the first call that needs it on that stream and grown by a later call
+ *     that needs more; buffers it grows out of stay allocated (a graph
+ *     captured earlier may still use them) until q8_release() frees them
+ *     all.  Allocation cannot be recorded into a graph, so a call made while
+ *     its stream is being captured and that would have to allocate or grow
+ *     the workspace returns Q8_ERR_INVALID and enqueues nothing: make one
+ *     eager call of the same (or a larger) shape on that stream first.
+ *     Captured calls replay correctly: their arrival counters return to zero
  *     inside every launch, and no call records a memset.
  */
 #ifndef Q8_GEMV_H
@@ -235,8 +239,10 @@ const char *q8_status_string(q8_status s);
 /* The hipError_t behind the calling thread's most recent Q8_ERR_HIP (0 if none). */
 int q8_last_hip_error(void);
 
-/* Frees every library-owned workspace after synchronising the device(s) that
- * own one.  Safe to call at any time when no call is in flight. */
+/* Frees every library-owned workspace, including buffers a workspace grew out
+ * of, after synchronising the device(s) that own one.  Call it when no call is
+ * in flight and no captured graph that uses the workspaces will be replayed
+ * again.  */
 void q8_release(void);
 
 #ifdef __cplusplus

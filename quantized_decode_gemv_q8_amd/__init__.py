@@ -8,10 +8,13 @@ Importing this package loads nothing; the library is loaded on first use.
 from .binding import (  # noqa: F401
     EXPORTED,
     Q8Error,
+    q8_dot_f32,
     q8_dot_t,
+    q8_dot_t_f32,
     q8_last_hip_error,
     q8_matvec,
     q8_matvec_choose_plan,
+    q8_matvec_fused,
     q8_matvec_with_plan,
     q8_release,
     q8_status_string,

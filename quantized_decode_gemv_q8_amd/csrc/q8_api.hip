@@ -5,6 +5,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "q8_common.h"
 #include "q8_gemv.h"
@@ -48,6 +49,11 @@ struct Workspace {
 std::mutex g_mu;
 std::map<int, DevInfo> g_dev;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Buffers a workspace grew out of, with their device.  A graph captured
+// before the growth still holds their addresses, so they stay allocated until
+// q8_release().
+std::vector<std::pair<int, void *>> g_retired;
+
 
 q8_status current_device(int *dev, DevInfo *info) {
   hipError_t e = hipGetDevice(dev);
@@ -315,29 +321,32 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   return Q8_OK;
 }
 
-// Workspace of (device, stream), grown to at least the requested sizes.
+// Workspace of (device, stream), grown to at least the requested sizes.  A
+// workspace cannot grow while the stream is being captured (an allocation
+// cannot be recorded into a graph): such a call returns Q8_ERR_INVALID.  The
+// buffers it grows out of are retired, not freed (see g_retired).
 q8_status get_workspace(int dev, hipStream_t stream, size_t partial_words, size_t n_counters,
                         Workspace *out) {
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace &ws = g_ws[std::make_pair(dev, stream)];
+  if (ws.partial_words < partial_words || ws.n_counters < n_counters) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_status(e);
+    if (cs != hipStreamCaptureStatusNone) return Q8_ERR_INVALID;
+  }
   if (ws.partial_words < partial_words) {
-    if (ws.partial) {
-      hipError_t e = hipFree(ws.partial);  // synchronises with work still using it
-      ws.partial = nullptr;
-      ws.partial_words = 0;
-      if (e != hipSuccess) return hip_status(e);
-    }
+    if (ws.partial) g_retired.emplace_back(dev, ws.partial);
+    ws.partial = nullptr;
+    ws.partial_words = 0;
     hipError_t e = hipMalloc((void **)&ws.partial, partial_words * sizeof(float));
     if (e != hipSuccess) return hip_status(e);
     ws.partial_words = partial_words;
   }
   if (ws.n_counters < n_counters) {
-    if (ws.counters) {
-      hipError_t e = hipFree(ws.counters);
-      ws.counters = nullptr;
-      ws.n_counters = 0;
-      if (e != hipSuccess) return hip_status(e);
-    }
+    if (ws.counters) g_retired.emplace_back(dev, ws.counters);
+    ws.counters = nullptr;
+    ws.n_counters = 0;
     size_t n = n_counters < 4096 ? 4096 : n_counters;
     hipError_t e = hipMalloc((void **)&ws.counters, n * sizeof(uint32_t));
     if (e != hipSuccess) return hip_status(e);
@@ -602,6 +611,12 @@ void q8_release(void) {
     if (kv.second.counters) (void)hipFree(kv.second.counters);
   }
   g_ws.clear();
+  for (auto &r : g_retired) {
+    (void)hipSetDevice(r.first);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(r.second);
+  }
+  g_retired.clear();
   if (cur >= 0) (void)hipSetDevice(cur);
 }
 

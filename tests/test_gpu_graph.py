@@ -155,3 +155,63 @@ def test_dense_dot_t_f32_replay():
         assert err <= TOL, f"normalised error {err:.3e}"
 
     replay_and_compare(call, [torch.empty((M, N), dtype=torch.float32, device=DEV)], refresh, check_first)
+
+
+def test_graph_survives_workspace_growth_and_growth_under_capture_is_refused():
+    """A graph captured while the stream's workspace was small stays valid
+    after a later eager call on that stream grows the workspace (the buffers
+    it grew out of are retired, not freed), and a call that would have to grow
+    the workspace while the stream is being captured is refused with
+    Q8_ERR_INVALID before anything is enqueued."""
+    s = torch.cuda.Stream()
+    # small split-K call on a fresh stream: allocates that stream's workspace
+    A, W, S = workloads.q8_inputs(1, 1000, 600, (83, 1))
+    Ad, Wd, Sd = to_dev(A), to_dev(W), to_dev(S)
+    out = torch.empty((1, 600), dtype=torch.float32, device=DEV)
+    plan = {"vec": 4, "m_tile": 1, "workgroups": 16}
+    with torch.cuda.stream(s):
+        binding.q8_matvec_with_plan(Ad, Wd, Sd, plan, out=out)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.q8_matvec_with_plan(Ad, Wd, Sd, plan, out=out)
+    # a larger eager call on the same stream grows the workspace
+    A2, W2, S2 = workloads.q8_inputs(1, 8192, 28672, (83, 2))
+    big = torch.empty((1, 28672), dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(s):
+        binding.q8_matvec(to_dev(A2), to_dev(W2), to_dev(S2), out=big)
+    s.synchronize()
+    for r in range(REPLAYS):
+        Ad.copy_(to_dev(workloads.q8_inputs(1, 1000, 600, (83, 10 + r))[0]))
+        torch.cuda.synchronize()
+        print(f"[graph] replay {r} after growth", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        ref = torch.empty_like(out)
+        with torch.cuda.stream(s):
+            binding.q8_matvec_with_plan(Ad, Wd, Sd, plan, out=ref)
+        s.synchronize()
+        assert torch.equal(out, ref), f"replay {r} after the workspace grew differs from the eager call"
+    del g
+    # 8 rows on the matrix cores need far more partial space than the stream holds now
+    A3, W3, S3 = workloads.q8_inputs(8, 4096, 28672, (83, 3))
+    A3d, W3d, S3d = to_dev(A3), to_dev(W3), to_dev(S3)
+    out3 = torch.full((8, 28672), 5.0, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(binding.Q8Error) as ei:
+        with torch.cuda.graph(g2, stream=s):
+            binding.q8_matvec(A3d, W3d, S3d, out=out3)
+    assert ei.value.status == binding.Q8_ERR_INVALID
+    del g2
+    torch.cuda.synchronize()
+    assert bool((out3 == 5.0).all()), "a refused call must not write its output"
+    # the same call eagerly grows the workspace and succeeds
+    with torch.cuda.stream(s):
+        binding.q8_matvec(A3d, W3d, S3d, out=out3)
+    s.synchronize()
+    cols = np.unique(np.random.default_rng(3).integers(0, 28672, 128))
+    W3c, S3c = np.ascontiguousarray(W3[:, cols]), np.ascontiguousarray(S3[:, cols])
+    err = oracle.normalised_error(out3.cpu().numpy()[:, cols], oracle.q8_matvec(A3, W3c, S3c),
+                                  oracle.q8_normaliser(A3, W3c, S3c))
+    assert err <= TOL
