@@ -75,6 +75,26 @@ q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C,
                     int64_t M, int64_t K, int64_t N, void *stream);
 
 /*
+ * q8_matvec_noalloc -- q8_matvec that allocates nothing, for callers that
+ * cannot call hipMalloc (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, plan choice, kernels
+ * and results (bitwise) as q8_matvec.  Instead of the library's workspace it
+ * uses a fixed scratch array that every device the library runs on holds for
+ * the life of the process: 32 MiB of split-K partial sums and 64 KiB of
+ * arrival counters.  The counters are cleared once per device, on that
+ * device's first call (a fill kernel on `stream`), and every launch leaves
+ * them at zero again.  A call whose plan needs more partial space returns
+ * Q8_ERR_TOO_LARGE and enqueues nothing (for example the matrix-core product
+ * of 33..64 rows at N much above 28672); q8_matvec has no such limit.
+ * All calls on one device share the scratch array: calls that overlap in
+ * time on one device (on different streams, or concurrently from several
+ * threads) race and give wrong results; serialise them.
+ * Errors: as q8_matvec, plus Q8_ERR_TOO_LARGE for plans beyond the scratch.
+ */
+q8_status q8_matvec_noalloc(const float *A, const int8_t *W, const float *S, float *C,
+                            int64_t M, int64_t K, int64_t N, void *stream);
+
+/*
  * Launch plan of q8_matvec.  Every field 0 means "choose automatically".
  *   kind    Q8_PLAN_STREAM or Q8_PLAN_MATRIX (below); 0 picks one from the
  *           shape: the matrix cores, when allowed, above 16 rows; at 9..16
@@ -242,7 +262,7 @@ int q8_last_hip_error(void);
 /* Frees every library-owned workspace, including buffers a workspace grew out
  * of, after synchronising the device(s) that own one.  Call it when no call is
  * in flight and no captured graph that uses the workspaces will be replayed
- * again.  */
+ * again.  The scratch array of q8_matvec_noalloc is not freed. */
 void q8_release(void);
 
 #ifdef __cplusplus

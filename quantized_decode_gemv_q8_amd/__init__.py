@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     q8_matvec,
     q8_matvec_choose_plan,
     q8_matvec_fused,
+    q8_matvec_noalloc,
     q8_matvec_with_plan,
     q8_release,
     q8_status_string,

@@ -26,6 +26,7 @@ PLAN_MATRIX = 2
 #: Every symbol include/q8_gemv.h declares.
 EXPORTED = (
     "q8_matvec",
+    "q8_matvec_noalloc",
     "q8_matvec_with_plan",
     "q8_matvec_choose_plan",
     "q8_matvec_fused",
@@ -78,6 +79,8 @@ def load():
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.q8_matvec.argtypes = [p, p, p, p, i64, i64, i64, p]
     L.q8_matvec.restype = ctypes.c_int
+    L.q8_matvec_noalloc.argtypes = [p, p, p, p, i64, i64, i64, p]
+    L.q8_matvec_noalloc.restype = ctypes.c_int
     L.q8_matvec_with_plan.argtypes = [p, p, p, p, i64, i64, i64, ctypes.POINTER(Q8Plan), p]
     L.q8_matvec_with_plan.restype = ctypes.c_int
     L.q8_matvec_choose_plan.argtypes = [i64, i64, i64, i64, i64, i32, ctypes.POINTER(Q8Plan)]
@@ -182,6 +185,19 @@ def q8_matvec(A, W, S, out=None, stream=None):
                               M, K, N, _stream_handle(stream, A.device))
     if st != Q8_OK:
         raise Q8Error(st, "q8_matvec")
+    return out
+
+
+def q8_matvec_noalloc(A, W, S, out=None, stream=None):
+    """q8_matvec through the library's fixed scratch array instead of its
+    workspace: the call allocates nothing on the device (out must be given to
+    avoid torch's allocation).  Calls that overlap in time on one device race."""
+    M, K, N, out = _q8_args(A, W, S, out)
+    with torch.cuda.device(A.device):
+        st = load().q8_matvec_noalloc(A.data_ptr(), W.data_ptr(), S.data_ptr(), out.data_ptr(),
+                                      M, K, N, _stream_handle(stream, A.device))
+    if st != Q8_OK:
+        raise Q8Error(st, "q8_matvec_noalloc")
     return out
 
 

@@ -54,6 +54,15 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 // q8_release().
 std::vector<std::pair<int, void *>> g_retired;
 
+// Scratch of q8_matvec_noalloc, for callers that cannot allocate: arrival
+// counters (kScratchCounterWords words) followed by split-K partials
+// (kScratchPartialWords floats).  Every device the library runs on holds its
+// own copy until the process ends.  Host code reaches it only through the
+// per-device address that hipGetSymbolAddress returns (g_scratch).
+constexpr size_t kScratchCounterWords = 16384;                  // 64 KiB
+constexpr size_t kScratchPartialWords = ((size_t)32 << 20) / 4;  // 32 MiB
+static __device__ __align__(256) uint32_t scratch[kScratchCounterWords + kScratchPartialWords];
+std::map<int, uint32_t *> g_scratch;
 
 q8_status current_device(int *dev, DevInfo *info) {
   hipError_t e = hipGetDevice(dev);
@@ -359,9 +368,42 @@ q8_status get_workspace(int dev, hipStream_t stream, size_t partial_words, size_
   return Q8_OK;
 }
 
+// The allocation-free workspace of device `dev` (current): the file-scope
+// scratch array.  Its address is looked up once per device, and its counters
+// are cleared then with a fill kernel on `stream`; every launch leaves them at
+// zero again.
+q8_status scratch_workspace(int dev, hipStream_t stream, Workspace *out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  uint32_t *ptr = nullptr;
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) {
+    ptr = it->second;
+  } else {
+    hipError_t e = hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    e = q8::launch_zero_fill(ptr, kScratchCounterWords, stream);
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch[dev] = ptr;
+  }
+  out->counters = ptr;
+  out->n_counters = kScratchCounterWords;
+  out->partial = reinterpret_cast<float *>(ptr + kScratchCounterWords);
+  out->partial_words = kScratchPartialWords;
+  return Q8_OK;
+}
+
+// The workspace of a call: the library's per-(device, stream) one, or the
+// scratch array (no_alloc), which refuses sizes beyond its capacity.
+q8_status call_workspace(bool no_alloc, int dev, hipStream_t stream, size_t partial_words, size_t n_counters,
+                         Workspace *out) {
+  if (!no_alloc) return get_workspace(dev, stream, partial_words, n_counters, out);
+  if (partial_words > kScratchPartialWords || n_counters > kScratchCounterWords) return Q8_ERR_TOO_LARGE;
+  return scratch_workspace(dev, stream, out);
+}
+
 // The fused matvec: every sibling's C = alpha * (A x dequant(W, S)) (+ corr[m] * C).
 q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64_t M, int64_t K, int64_t N,
-                     float alpha, const float *corr, const q8_plan *req, void *stream_v) {
+                     float alpha, const float *corr, const q8_plan *req, void *stream_v, bool no_alloc = false) {
   if (!plan_is_valid_shape(M, K, N) || sib == nullptr || n_sib < 1 || n_sib > q8::kMaxSiblings)
     return Q8_ERR_INVALID;
   if (M == 0 || N == 0) return Q8_OK;
@@ -415,7 +457,7 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
     const int64_t passes = ceil_div(M, rows);
     const size_t part =
         g.splits > 1 ? (size_t)(passes * g.n_tiles * g.splits * rows * q8::kGemmTileCols) : 1;
-    st = get_workspace(dev, stream, part, (size_t)(passes * g.n_tiles) * q8::kCounterStride, &ws);
+    st = call_workspace(no_alloc, dev, stream, part, (size_t)(passes * g.n_tiles) * q8::kCounterStride, &ws);
     if (st != Q8_OK) return st;
     g.partial = ws.partial;
     g.counters = ws.counters;
@@ -447,8 +489,8 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
   const int64_t slab_chunks = L.m_chunks < kMaxGridY ? L.m_chunks : kMaxGridY;
   {
     Workspace ws;
-    st = get_workspace(dev, stream, (size_t)(slab_chunks * L.n_tiles * L.cmax * pl.m_tile * 64 * pl.vec),
-                       (size_t)(slab_chunks * L.n_tiles) * q8::kCounterStride, &ws);
+    st = call_workspace(no_alloc, dev, stream, (size_t)(slab_chunks * L.n_tiles * L.cmax * pl.m_tile * 64 * pl.vec),
+                        (size_t)(slab_chunks * L.n_tiles) * q8::kCounterStride, &ws);
     if (st != Q8_OK) return st;
     a.partial = ws.partial;
     a.counters = ws.counters;
@@ -473,9 +515,9 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
 }
 
 q8_status matvec_impl(const float *A, const int8_t *W, const float *S, float *C, int64_t M,
-                      int64_t K, int64_t N, const q8_plan *req, void *stream) {
+                      int64_t K, int64_t N, const q8_plan *req, void *stream, bool no_alloc = false) {
   const q8_sibling one{W, S, C};
-  return fused_impl(A, &one, 1, M, K, N, 1.0f, nullptr, req, stream);
+  return fused_impl(A, &one, 1, M, K, N, 1.0f, nullptr, req, stream, no_alloc);
 }
 
 // Dense f32 dot (B [K,N]) or dot_t (B [N,K]) through the epilogue.
@@ -521,6 +563,11 @@ extern "C" {
 q8_status q8_matvec(const float *A, const int8_t *W, const float *S, float *C, int64_t M,
                     int64_t K, int64_t N, void *stream) {
   return matvec_impl(A, W, S, C, M, K, N, nullptr, stream);
+}
+
+q8_status q8_matvec_noalloc(const float *A, const int8_t *W, const float *S, float *C, int64_t M,
+                            int64_t K, int64_t N, void *stream) {
+  return matvec_impl(A, W, S, C, M, K, N, nullptr, stream, true);
 }
 
 q8_status q8_matvec_with_plan(const float *A, const int8_t *W, const float *S, float *C,

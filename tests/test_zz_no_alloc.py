@@ -1,0 +1,76 @@
+"""q8_matvec_noalloc: the allocation-free variant of q8_matvec.
+
+It runs the same plans and kernels as q8_matvec with the split-K workspace
+taken from the library's fixed scratch array, so its results must equal
+q8_matvec's bit for bit, on consecutive calls that reuse the scratch (the
+second smaller than the first), on both the per-row stream and the
+matrix-core product, and meet the oracle's bar.  A plan that needs more
+partial space than the scratch holds is refused before anything is enqueued.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_decode_gemv_q8_amd import binding, workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-5
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def run_pair(M, K, N, seed):
+    A, W, S = workloads.q8_inputs(M, K, N, seed)
+    Ad, Wd, Sd = to_dev(A), to_dev(W), to_dev(S)
+    ref = binding.q8_matvec(Ad, Wd, Sd)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    binding.q8_matvec_noalloc(Ad, Wd, Sd, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), f"noalloc differs from q8_matvec at M={M} K={K} N={N}"
+    # the oracle's bar on sampled columns (all of them for small N)
+    cols = np.arange(N) if N <= 2048 else np.unique(np.random.default_rng(seed[-1]).integers(0, N, 256))
+    Wc, Sc = np.ascontiguousarray(W[:, cols]), np.ascontiguousarray(S[:, cols])
+    err = oracle.normalised_error(out.cpu().numpy()[:, cols], oracle.q8_matvec(A, Wc, Sc),
+                                  oracle.q8_normaliser(A, Wc, Sc))
+    assert err <= TOL, f"normalised error {err:.3e}"
+
+
+@pytest.mark.parametrize("first,second", [
+    ((1, 8192, 28672), (1, 4100, 5000)),    # split-K stream: the headline shape, then a ragged smaller one
+    ((4, 4100, 5000), (2, 1000, 300)),      # several rows per pass, then a short K
+    ((16, 4096, 8192), (8, 1000, 1024)),    # matrix-core product, then a smaller one
+])
+def test_noalloc_matches_q8_matvec_on_consecutive_calls(first, second):
+    print(f"[no_alloc] {first} then {second}", flush=True)
+    run_pair(*first, (71, 1))
+    run_pair(*second, (71, 2))
+
+
+def test_noalloc_refuses_plans_beyond_the_scratch():
+    # 200 rows on the per-row stream (25 chunks of 8 rows) over 32 column
+    # tiles with 16 contributors each need 25 * 32 * 16 * 8 * 128 floats
+    # (50 MiB) of partials, above the 32 MiB scratch.
+    M, K, N = 200, 4096, 4096
+    A, W, S = workloads.q8_inputs(M, K, N, (71, 3))
+    Ad, Wd, Sd = to_dev(A), to_dev(W), to_dev(S)
+    out = torch.full((M, N), 7.0, dtype=torch.float32, device=DEV)
+    with pytest.raises(binding.Q8Error) as ei:
+        binding.q8_matvec_noalloc(Ad, Wd, Sd, out=out)
+    assert ei.value.status == binding.Q8_ERR_TOO_LARGE
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()), "a refused call must not write its output"
+    # the allocating entry point serves the same shape
+    binding.q8_matvec(Ad, Wd, Sd, out=out)
+    torch.cuda.synchronize()
+    rows = [0, 99, 199]
+    cols = np.unique(np.random.default_rng(5).integers(0, N, 128))
+    Wc, Sc = np.ascontiguousarray(W[:, cols]), np.ascontiguousarray(S[:, cols])
+    Ar = np.ascontiguousarray(A[rows])
+    err = oracle.normalised_error(out.cpu().numpy()[rows][:, cols], oracle.q8_matvec(Ar, Wc, Sc),
+                                  oracle.q8_normaliser(Ar, Wc, Sc))
+    assert err <= TOL
