@@ -163,11 +163,12 @@ q8_status q8_matvec_with_plan(const float *A, const int8_t *W, const float *S, f
 /*
  * Fused matvec: sibling projections and the elementwise epilogue.
  *
- * "dot and tensor cores", section "The fused epilogue": a product that only
- * feeds an elementwise statement is updated per element as it is written out
- * instead of being stored and swept again (the page's examples scale a
- * product, s = s * scale, and rescale an accumulator while adding a product,
- * acc = acc * corr + dot(p, v)).  Here, for every sibling g:
+ * "dot and tensor cores", section "The fused epilogue": the elementwise
+ * statement that consumes a product runs on each element while the product
+ * is written, with no second pass over a stored result (the page's examples
+ * multiply a product by a scale, s = s * scale, and multiply an existing
+ * accumulator by a factor before adding a product, acc = acc * corr +
+ * dot(p, v)).  Here, for every sibling g:
  *
  *   C_g[m,n] = alpha * P_g[m,n] + corr[m] * C_g[m,n]     (corr != NULL)
  *   C_g[m,n] = alpha * P_g[m,n]                          (corr == NULL)

@@ -15,15 +15,16 @@ Sources (Phobos documentation pages):
     C[0,n] = sum_k A[0,k] * W[k,n] * S[k/32, n].
   * same page, section "Factoring out the scale": the per-block identity
     sum_{k in b} A[k] W[k,n] S[b,n] = S[b,n] * sum_{k in b} A[k] W[k,n].
-  * same page, section "Bounds": N need not be a multiple of the tile, the K
-    loop is whole blocks plus one masked remainder.
+  * same page, section "Bounds": N need not be a multiple of the tile, and
+    when K is not a multiple of 32 the last block is short (its missing rows
+    are masked out).
   * "dot and tensor cores" (docs/language/dot-and-tensor-cores), the table of
     built-ins: dot_t(a, b) with a [M,K], b [N,K] computes a @ b^T; section
     "Hardware paths": i8 operands accumulate in i32, f32 operands in f32;
     section "The k loop": dot(a, b) with a [M,K], b [K,N] is a @ b,
-    accumulated over panels of K; section "The fused epilogue": a product
-    feeding an elementwise statement is updated as it is written out (scale,
-    and rescale-and-add).
+    accumulated over panels of K; section "The fused epilogue": the
+    elementwise statement that consumes a product (a scale, or a rescale of
+    the existing value followed by an add) runs as the product is written.
 
 Every function is pinned by tests in ``tests/test_oracle.py`` against exact
 rational arithmetic, closed forms, library special cases and hand-derived

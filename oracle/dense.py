@@ -11,9 +11,10 @@ Page: "dot and tensor cores".
     changes rounding, so the f64 reference is the plain definition.
   * Section "Hardware paths": f32 operands with an f32 accumulator take the
     FMA path (full f32 products, no operand rounding).
-  * Section "The fused epilogue": a product feeding an elementwise statement
-    (s = s * scale; acc = acc * corr + dot) is updated as it is written; the
-    epilogue is the same y = alpha * P + corr[m] * C_old as the Q8_0 one.
+  * Section "The fused epilogue": the elementwise statement that consumes a
+    product (s = s * scale; acc = acc * corr + dot) runs as the product is
+    written; the epilogue is the same y = alpha * P + corr[m] * C_old as the
+    Q8_0 one.
 
 Readings taken where the page is silent: layouts are
 dense row-major; K == 0 gives a zero product; C is overwritten unless the

@@ -134,11 +134,12 @@ def normalised_error(C_test, C_ref, D):
 def q8_epilogue(P, alpha=1.0, corr=None, C_old=None):
     """The fused epilogue of "dot and tensor cores" ("The fused epilogue"), f64.
 
-    A product that only feeds an elementwise statement is updated as it is
-    written out; the page's statements scale a product (s = s * scale) and
-    rescale an accumulator while adding a product (acc = acc * corr + dot).
-    Here y[m,n] = alpha * P[m,n] + corr[m] * C_old[m,n], or alpha * P[m,n]
-    without row factors.
+    The page lets the elementwise statement that consumes a product run while
+    the product is being written, with no separate pass over the result; its
+    examples multiply a product by a scale (s = s * scale) and multiply an
+    existing accumulator by a factor before adding a product (acc = acc * corr
+    + dot).  Here y[m,n] = alpha * P[m,n] + corr[m] * C_old[m,n], or
+    alpha * P[m,n] without row factors.
     """
     y = float(alpha) * np.asarray(P, dtype=np.float64)
     if corr is not None:

@@ -4,7 +4,8 @@
 // Operation: "Q8_0 matvec" page, sections "The tensors" (definition and
 // layouts), "Factoring out the scale" (one scale multiply per block and
 // column, applied to the block's unscaled partial) and "Bounds" (ragged N is
-// masked; the K loop is whole blocks plus one masked remainder).
+// masked, and a K that is not a multiple of 32 ends in a short last block
+// whose missing rows contribute nothing).
 //
 // Work decomposition (a CDNA design, not the pages' 64-column CTA tile):
 //   * W is cut into column tiles of 64*VEC columns and, along K, into groups of

@@ -440,3 +440,77 @@ def test_mutant_epilogue_is_caught(mutant):
     corr = np.array([2.0, -1.0, 0.5], np.float32)
     C_old = rng.standard_normal((3, 4)).astype(np.float32)
     assert not (pin_golden_epilogue(mutant) and pin_exact_epilogue(mutant, A, W, S, 0.5, corr, C_old))
+
+
+# ------------------------------------------- fused siblings: hand-derived pin
+
+def _fused_fixture():
+    with open(os.path.join(GOLDEN, "q8_fused_hand_example.json")) as f:
+        g = json.load(f)
+    inp = g["inputs"]
+    A = np.array(inp["A"], np.float32)
+    sib = [(np.array(s["W"], np.int8), np.array(s["S"], np.float32)) for s in inp["siblings"]]
+    olds = [np.array(s["C_old"], np.float32) for s in inp["siblings"]]
+    corr = np.array(inp["corr"], np.float32)
+    return A, sib, inp["alpha"], corr, olds, g
+
+
+def pin_golden_fused(fused=None, norm=None):
+    """q8_matvec_fused and q8_fused_normaliser against the hand-derived
+    two-sibling example (negative alpha, row factors of both signs)."""
+    fused = fused or oracle.q8_matvec_fused
+    norm = norm or oracle.q8_fused_normaliser
+    A, sib, alpha, corr, olds, g = _fused_fixture()
+    ys = fused(A, sib, alpha, corr, olds)
+    ok = len(ys) == len(sib)
+    ok = ok and all(np.array_equal(y, np.array(e)) for y, e in zip(ys, g["expected_y"]))
+    ok = ok and all(np.array_equal(oracle.q8_matvec(A, W, S), np.array(e)) for (W, S), e in zip(sib, g["expected_P"]))
+    ok = ok and all(np.array_equal(norm(A, W, S, alpha, corr, old), np.array(e))
+                    for (W, S), old, e in zip(sib, olds, g["expected_D"]))
+    return bool(ok)
+
+
+def test_golden_fused_hand_example():
+    assert pin_golden_fused()
+
+
+def _mut_fused_swapped_olds(A, siblings, alpha=1.0, corr=None, C_olds=None):
+    return oracle.q8_matvec_fused(A, siblings, alpha, corr, None if C_olds is None else C_olds[::-1])
+
+
+def _mut_fused_alpha_on_old(A, siblings, alpha=1.0, corr=None, C_olds=None):
+    out = []
+    for g, (W, S) in enumerate(siblings):
+        y = oracle.q8_matvec(A, W, S)
+        if corr is not None:
+            y = y + float(alpha) * np.asarray(corr, np.float64).reshape(-1, 1) * np.asarray(C_olds[g], np.float64)
+        out.append(y)
+    return out
+
+
+def _mut_fused_first_weights(A, siblings, alpha=1.0, corr=None, C_olds=None):
+    return oracle.q8_matvec_fused(A, [siblings[0]] * len(siblings), alpha, corr, C_olds)
+
+
+def _mut_norm_signed_corr(A, W, S, alpha=1.0, corr=None, C_old=None):
+    D = abs(float(alpha)) * oracle.q8_normaliser(A, W, S)
+    if corr is not None:
+        D = D + np.asarray(corr, np.float64).reshape(-1, 1) * np.asarray(C_old, np.float64)
+    return D
+
+
+def _mut_norm_signed_alpha(A, W, S, alpha=1.0, corr=None, C_old=None):
+    D = float(alpha) * oracle.q8_normaliser(A, W, S)
+    if corr is not None:
+        D = D + np.abs(np.asarray(corr, np.float64).reshape(-1, 1) * np.asarray(C_old, np.float64))
+    return D
+
+
+@pytest.mark.parametrize("mutant", [_mut_fused_swapped_olds, _mut_fused_alpha_on_old, _mut_fused_first_weights])
+def test_mutant_fused_siblings_is_caught(mutant):
+    assert not pin_golden_fused(fused=mutant)
+
+
+@pytest.mark.parametrize("mutant", [_mut_norm_signed_corr, _mut_norm_signed_alpha])
+def test_mutant_fused_normaliser_is_caught(mutant):
+    assert not pin_golden_fused(norm=mutant)

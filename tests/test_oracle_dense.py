@@ -165,3 +165,55 @@ def test_mutant_transposed_operand_is_caught():
 
 def test_mutant_signed_normaliser_is_caught():
     assert not pin_golden(norm=_mut_signed_norm)
+
+
+# ------------------------------------------ fused epilogue: hand-derived pin
+
+def pin_golden_fused(fused=od.dense_fused, norm=od.dense_fused_normaliser):
+    """dense_fused and dense_fused_normaliser against the hand-derived example
+    with a negative alpha and row factors of both signs, for dot and dot_t."""
+    with open(os.path.join(GOLDEN, "dense_hand_example.json")) as f:
+        g = json.load(f)
+    A = np.array(g["A"], np.float32)
+    f_ = g["fused"]
+    corr = np.array(f_["corr"], np.float32)
+    old = np.array(f_["C_old"], np.float32)
+    ok = True
+    for B, tr, key in ((np.array(g["B_nk"], np.float32), True, "dot_t"), (np.array(g["B_kn"], np.float32), False, "dot")):
+        ok &= np.array_equal(fused(A, B, tr, f_["alpha"], corr, old), np.array(f_[f"expected_{key}_y"]))
+        ok &= np.array_equal(norm(A, B, tr, f_["alpha"], corr, old), np.array(f_[f"expected_{key}_D"]))
+    return bool(ok)
+
+
+def test_golden_fused_hand_example():
+    assert pin_golden_fused()
+
+
+def _mut_fused_alpha_on_old(A, B, transposed=False, alpha=1.0, corr=None, C_old=None):
+    P = od.dot_t_f32(A, B) if transposed else od.dot_f32(A, B)
+    return P + float(alpha) * np.asarray(corr, np.float64).reshape(-1, 1) * np.asarray(C_old, np.float64)
+
+
+def _mut_fused_corr_by_column(A, B, transposed=False, alpha=1.0, corr=None, C_old=None):
+    P = od.dot_t_f32(A, B) if transposed else od.dot_f32(A, B)
+    return float(alpha) * P + np.asarray(corr, np.float64).reshape(1, -1) * np.asarray(C_old, np.float64)
+
+
+def _mut_fused_norm_signed_corr(A, B, transposed=False, alpha=1.0, corr=None, C_old=None):
+    D = abs(float(alpha)) * od.dense_normaliser(A, B, transposed)
+    return D + np.asarray(corr, np.float64).reshape(-1, 1) * np.asarray(C_old, np.float64)
+
+
+def _mut_fused_norm_signed_alpha(A, B, transposed=False, alpha=1.0, corr=None, C_old=None):
+    D = float(alpha) * od.dense_normaliser(A, B, transposed)
+    return D + np.abs(np.asarray(corr, np.float64).reshape(-1, 1) * np.asarray(C_old, np.float64))
+
+
+@pytest.mark.parametrize("mutant", [_mut_fused_alpha_on_old, _mut_fused_corr_by_column])
+def test_mutant_dense_fused_is_caught(mutant):
+    assert not pin_golden_fused(fused=mutant)
+
+
+@pytest.mark.parametrize("mutant", [_mut_fused_norm_signed_corr, _mut_fused_norm_signed_alpha])
+def test_mutant_dense_fused_normaliser_is_caught(mutant):
+    assert not pin_golden_fused(norm=mutant)
