@@ -15,14 +15,17 @@ the timed region (one launch per step, issued back to back).  A second pass
 records events around every single launch; its percentiles (`per_launch_us`)
 show the spread but include the event packets' own overhead.
 
-The default warm-up is long (400 launches, about 18 ms) because the device
-needs roughly 10 ms of sustained load before the kernel settles at its
-steady-state duration.
+The warm-up is at least 400 launches and at least 20 ms of device time
+(whichever is longer; `warmup_used` reports both) because the device needs
+roughly 10 ms of sustained load before the kernel settles at its steady-state
+duration.
 
 `--graph` submits the timed steps as one captured HIP graph instead of one
 call per step; it matters only for kernels shorter than a Python call.
-`--workload` picks another workload of workloads.py (the dense ones report
-TFLOP/s against the f32 matrix peak).
+`--workload` picks another workload of workloads.py.  The dense ones report
+`value` in TFLOP/s of f32 products; their `roofline` is the bf16 matrix-core
+issue rate the exact three-part split runs at (six bf16 part products per f32
+product) against the bf16 peak, and `f32_equivalent` gives the f32 view.
 """
 
 import argparse
@@ -82,36 +85,61 @@ def measured_traffic(workload, kernel_path):
     return rec.get("bytes_per_launch")
 
 
-def time_steps(launch, steps, warmup, n_copies, torch):
-    """Whole-job pass: `warmup` untimed steps, then `steps` back-to-back launches
-    bracketed by synchronisation; returns (wall seconds, HIP-event seconds)."""
+WARMUP_FLOOR_MS = 20.0  # the device needs about 10 ms of sustained load to settle
+
+
+def warm_up(launch, warmup, n_copies, torch):
+    """At least `warmup` untimed launches, and more until WARMUP_FLOOR_MS of
+    device time have passed since the first (events on the launch stream);
+    returns (launches, milliseconds)."""
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        launch(i % n_copies)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    n = 0
+    for _ in range(warmup):
+        launch(n % n_copies)
+        n += 1
+    while True:
+        t1.record(stream)
+        t1.synchronize()
+        ms = t0.elapsed_time(t1)
+        if ms >= WARMUP_FLOOR_MS:
+            return n, ms
+        for _ in range(16):
+            launch(n % n_copies)
+            n += 1
+
+
+def time_steps(launch, steps, warmup, n_copies, torch):
+    """Whole-job pass: the warm-up of warm_up(), then `steps` back-to-back
+    launches bracketed by synchronisation; returns (wall seconds, HIP-event
+    seconds, (warm-up launches, warm-up ms))."""
+    stream = torch.cuda.current_stream()
+    wu = warm_up(launch, warmup, n_copies, torch)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_start.record(stream)
     for i in range(steps):
-        launch((warmup + i) % n_copies)
+        launch((wu[0] + i) % n_copies)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, t_start.elapsed_time(t_end) * 1e-3
+    return wall, t_start.elapsed_time(t_end) * 1e-3, wu
 
 
 def time_steps_graph(launch, steps, warmup, n_copies, torch):
     """The same pass with the timed steps submitted as one HIP graph: the
     `steps` launches are captured once on a side stream (after eager warm-up
-    launches there, which also allocate the workspace), replayed once untimed,
-    then replayed once inside the timed region.  The warm-up launches and the
-    untimed replay together make `warmup` untimed steps when warmup >= steps.
-    Returns (wall seconds, HIP-event seconds) of the timed replay."""
+    launches there, which also allocate the workspace, for at least
+    WARMUP_FLOOR_MS), replayed once untimed, then replayed once inside the
+    timed region.  Returns (wall seconds, HIP-event seconds, (warm-up
+    launches, warm-up ms)) of the timed replay."""
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
-        for i in range(max(warmup - steps, 1)):
-            launch(i % n_copies)
+        wu = warm_up(launch, max(warmup - steps, 1), n_copies, torch)
     side.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
@@ -129,7 +157,7 @@ def time_steps_graph(launch, steps, warmup, n_copies, torch):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     del g
-    return wall, t_start.elapsed_time(t_end) * 1e-3
+    return wall, t_start.elapsed_time(t_end) * 1e-3, wu
 
 
 def time_kernels(launch, steps, n_copies, torch):
@@ -210,6 +238,42 @@ def cpu_baseline(wl, A, W, S, budget_s=12.0):
         "cpu_model": _cpu_model(),
         "sample": f"f64 factored oracle on the whole M={wl.M} K={wl.K} N={wl.N} workload (copy 0), "
                   f"{n} calls in {total:.1f} s; BLAS threads {threads}, numpy upcasts single-threaded",
+    }
+
+
+def cpu_baseline_fused(wl, A, Ws, Ss, budget_s=12.0):
+    """The oracle's sibling projections on the whole fused workload (copy 0)."""
+    import oracle
+
+    sib = list(zip(Ws, Ss))
+    n, total = _time_oracle(lambda: oracle.q8_matvec_fused(A, sib), budget_s)
+    threads = _blas_threads()
+    return {
+        "value": round(wl.algorithmic_bytes() * n / total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "sample": f"f64 oracle of {wl.siblings} siblings on the whole M={wl.M} K={wl.K} N={wl.N} workload "
+                  f"(copy 0), {n} calls in {total:.1f} s; BLAS threads {threads}",
+    }
+
+
+def cpu_baseline_dot_t(wl, A, W, budget_s=12.0):
+    """The oracle's exact int64 dot_t on the whole workload (copy 0), in GB/s
+    of the workload's algorithmic bytes.  numpy's integer matmul runs on one
+    thread (it has no BLAS path)."""
+    import oracle
+
+    n, total = _time_oracle(lambda: oracle.dot_t(A, W), budget_s)
+    return {
+        "value": round(wl.algorithmic_bytes() * n / total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "sample": f"int64 oracle on the whole M={wl.M} K={wl.K} N={wl.N} dot_t (copy 0), {n} calls in {total:.1f} s; "
+                  "numpy integer matmul, single-threaded",
     }
 
 
@@ -444,7 +508,7 @@ def main():
         return
 
     timer = time_steps_graph if args.graph else time_steps
-    wall, gpu_s = timer(launch, args.steps, args.warmup, n_copies, torch)
+    wall, gpu_s, (wu_n, wu_ms) = timer(launch, args.steps, args.warmup, n_copies, torch)
     per = time_kernels(launch, args.steps, n_copies, torch)
     nbytes = wl.algorithmic_bytes()
     ms_per_step = wall * 1e3 / args.steps
@@ -458,7 +522,7 @@ def main():
 
     unfused = None
     if wl.op == "q8_fused":
-        wall_u, gpu_u = time_steps(launch_unfused, args.steps, args.warmup // 4, n_copies, torch)
+        wall_u, gpu_u, _ = time_steps(launch_unfused, args.steps, args.warmup // 4, n_copies, torch)
         unfused = {"launches_per_step": wl.siblings, "step_us_events": round(gpu_u * 1e6 / args.steps, 3),
                    "value": round(nbytes * args.steps / wall_u / 1e9, 2)}
         print(f"[bench] unfused (one q8_matvec per sibling): {gpu_u * 1e6 / args.steps:.2f} us/step",
@@ -480,6 +544,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_used": {"launches": wu_n, "device_ms": round(wu_ms, 2), "floor_ms": WARMUP_FLOOR_MS},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -490,12 +555,15 @@ def main():
                    "rotated_copies": n_copies,
                    "algorithmic_bytes_per_step": nbytes, "plan": used_plan,
                    **({"algorithmic_flops_per_step": wl.algorithmic_flops()} if dense else {})},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F32_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / F32_MFMA_PEAK_TFLOPS, 4), "traffic": traffic}
+        "roofline": {"bound": "mfma", "achieved": round(DENSE_BF16_PRODUCTS * achieved, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(DENSE_BF16_PRODUCTS * achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "dtype": "bf16 (f32 operands split exactly into three bf16 parts, six part products each)"}
         if dense else
         {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "pct_of_peak": round(100.0 * value / (F32_MFMA_PEAK_TFLOPS if dense else HBM_PEAK_GBS), 2),
+        "pct_of_peak": round(100.0 * (DENSE_BF16_PRODUCTS * value / BF16_MFMA_PEAK_TFLOPS if dense else
+                                      value / HBM_PEAK_GBS), 2),
         "launch_us": round(launch_s * 1e6, 3),
         "submission": "one HIP graph of the timed steps" if args.graph else "one call per step",
         "per_launch_us": {"mean": round(float(np.mean(per)) * 1e3, 3), "median": round(float(np.median(per)) * 1e3, 3),
@@ -508,17 +576,23 @@ def main():
     if unfused is not None:
         result["unfused"] = unfused
     if dense:
-        # Hardware view of the same launches: bf16 MFMA flops issued against the bf16 peak.
-        issued = DENSE_BF16_PRODUCTS * achieved
-        result["bf16_mfma_issue"] = {"achieved": round(issued, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                     "frac": round(issued / BF16_MFMA_PEAK_TFLOPS, 4),
-                                     "bf16_products_per_f32_product": DENSE_BF16_PRODUCTS}
-    if not args.no_cpu_baseline and wl.op == "q8":
+        # The same launches counted as f32 products: against the f32 matrix
+        # peak, and against the ceiling of the bf16 split (bf16 peak / 6).
+        result["f32_equivalent"] = {"achieved": round(achieved, 2), "unit": "TFLOP/s",
+                                    "f32_matrix_peak": F32_MFMA_PEAK_TFLOPS,
+                                    "vs_f32_matrix_peak": round(achieved / F32_MFMA_PEAK_TFLOPS, 4),
+                                    "split_ceiling": round(BF16_MFMA_PEAK_TFLOPS / DENSE_BF16_PRODUCTS, 1),
+                                    "bf16_products_per_f32_product": DENSE_BF16_PRODUCTS}
+    if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, A0, W0, S0)
-    elif not args.no_cpu_baseline and dense:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline_dense(wl, A0, B0, alpha)
+        if wl.op == "q8":
+            result["cpu_baseline"] = cpu_baseline(wl, A0, W0, S0)
+        elif wl.op == "q8_fused":
+            result["cpu_baseline"] = cpu_baseline_fused(wl, A0, W0s, S0s)
+        elif dense:
+            result["cpu_baseline"] = cpu_baseline_dense(wl, A0, B0, alpha)
+        else:
+            result["cpu_baseline"] = cpu_baseline_dot_t(wl, A0, W0)
     print(json.dumps(result), flush=True)
 
 

@@ -1,5 +1,8 @@
 // C ABI of the Q8_0 matvec / i8 dot_t library: validation, launch planning,
 // the split-K workspace, and dispatch.  Declared in include/q8_gemv.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <map>
@@ -21,6 +24,24 @@ q8_status hip_status(hipError_t e) {
   if (e == hipSuccess) return Q8_OK;
   t_last_hip_error = (int)e;
   return Q8_ERR_HIP;
+}
+
+// Plan log: with the environment variable Q8_LOG=debug, every call prints
+// one line on stderr naming the kernel path and launch plan it chose and, when
+// it did not take the fastest path for its kind of problem, why (the
+// analogue of the pages' PHOBOS_LOG for dots that fall back).
+bool log_debug() {
+  const char *v = getenv("Q8_LOG");
+  return v != nullptr && strcmp(v, "debug") == 0;
+}
+
+void log_line(const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "q8: %s\n", buf);
 }
 
 constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // 32-bit signed element offsets
@@ -243,8 +264,18 @@ bool finish_gemm_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan 
 
 // matrix_ok: the call may use the matrix-core path (one weight set, plain
 // epilogue).
+// Why a plan did not take the matrix cores, wider lanes or more tiles
+// (empty when nothing fell back); for the plan log.
+struct PlanNotes {
+  const char *matrix = "";  // the matrix-core product was not used
+  const char *lanes = "";   // narrower than 8-byte lanes
+};
+
 q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w_align, int64_t s_align,
-                       int32_t num_cus, bool matrix_ok, const q8_plan *req, q8_plan *out) {
+                       int32_t num_cus, bool matrix_ok, const q8_plan *req, q8_plan *out,
+                       PlanNotes *notes = nullptr) {
+  PlanNotes local;
+  PlanNotes &nt = notes ? *notes : local;
   q8_plan pl = req ? *req : q8_plan{0, 0, 0, 0, 0};
   if (pl.kind != 0 && pl.kind != Q8_PLAN_STREAM && pl.kind != Q8_PLAN_MATRIX) return Q8_ERR_INVALID;
   // The matrix kernel reads A through a buffer descriptor with 32-bit byte
@@ -281,11 +312,21 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   const bool matrix_pays = (M > 16) || (M >= 9 && gemm_quarter) || (M >= 5 && gemm_3_8ths) ||
                            (M >= 3 && K * N >= ((int64_t)1 << 25) && gemm_fills) ||
                            (M == 2 && K * N >= ((int64_t)1 << 27) && gemm_fills);
-  if (pl.kind == 0)
+  if (pl.kind == 0) {
     pl.kind = (matrix_fits && matrix_pays && M >= Q8_MATRIX_MIN_ROWS && pl.vec == 0 && pl.m_tile == 0 &&
                pl.workgroups == 0)
                   ? Q8_PLAN_MATRIX
                   : Q8_PLAN_STREAM;
+    if (pl.kind == Q8_PLAN_STREAM && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0) {
+      nt.matrix = !matrix_ok               ? "matrix cores serve one weight set with the plain epilogue"
+                  : N % 16 != 0            ? "matrix cores need N % 16 == 0"
+                  : w_align % 16 != 0 || s_align % 16 != 0 ? "matrix cores need 16-byte aligned W and S"
+                  : !matrix_a_fits         ? "matrix cores need A below 2^31 bytes"
+                  : !matrix_shape          ? "too many K splits for the matrix-core grid"
+                  : pl.vec != 0 || pl.m_tile != 0 || pl.workgroups != 0 ? "stream fields set in the plan"
+                                           : "too few rows or too small a W for the matrix cores to pay";
+    }
+  }
   if (pl.kind == Q8_PLAN_MATRIX) {
     if (matrix_shape && !matrix_a_fits) return Q8_ERR_TOO_LARGE;
     if (pl.waves != 0 && pl.waves != q8::kGemmWaves) return Q8_ERR_INVALID;
@@ -316,9 +357,14 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
       }
     }
     if (pl.vec == 0) return Q8_ERR_INVALID;
+    if (pl.vec < 8 && 8 * pl.m_tile <= 16)
+      nt.lanes = N % 8 != 0 ? "N % 8 != 0 narrows the lanes" : "W or S alignment narrows the lanes";
     if (pl.vec == 8 && vec_fits(4, N, w_align, s_align) && K > 0) {
       const int64_t units8 = n_sib * ceil_div(N, 64 * 8) * ceil_div(ceil_div(K, kBlock), q8::kWaves);
-      if (units8 < 3 * (int64_t)num_cus) pl.vec = 4;
+      if (units8 < 3 * (int64_t)num_cus) {
+        pl.vec = 4;
+        nt.lanes = "fewer than three 8-byte-lane units per CU: 4-byte lanes halve the combine";
+      }
     }
   }
   if (pl.vec != 16 && pl.vec != 8 && pl.vec != 4 && pl.vec != 2 && pl.vec != 1) return Q8_ERR_INVALID;
@@ -435,8 +481,21 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
 
   q8_plan pl;
   const bool plain = n_sib == 1 && alpha == 1.0f && corr == nullptr;
-  st = resolve_plan(M, K, N, n_sib, w_align, s_align, info.cus, plain, req, &pl);
+  PlanNotes notes;
+  st = resolve_plan(M, K, N, n_sib, w_align, s_align, info.cus, plain, req, &pl, &notes);
   if (st != Q8_OK) return st;
+  if (log_debug()) {
+    if (pl.kind == Q8_PLAN_MATRIX)
+      log_line("%s M=%lld K=%lld N=%lld: matrix cores, %d workgroups (%lld K splits)%s",
+               no_alloc ? "matvec_noalloc" : "matvec", (long long)M, (long long)K, (long long)N, pl.workgroups,
+               (long long)(pl.workgroups / ceil_div(N, q8::kGemmTileCols)), req ? " (explicit plan)" : "");
+    else
+      log_line("%s M=%lld K=%lld N=%lld siblings=%lld: stream, vec %d, m_tile %d, %d workgroups%s%s%s%s%s",
+               no_alloc ? "matvec_noalloc" : n_sib > 1 || !plain ? "matvec_fused" : "matvec", (long long)M,
+               (long long)K, (long long)N, (long long)n_sib, pl.vec, pl.m_tile, pl.workgroups,
+               req ? " (explicit plan)" : "", *notes.matrix ? "; not on the matrix cores: " : "", notes.matrix,
+               *notes.lanes ? "; " : "", notes.lanes);
+  }
 
   if (pl.kind == Q8_PLAN_MATRIX) {
     q8::GemmArgs g;
@@ -542,6 +601,10 @@ q8_status dense_impl(const float *A, const float *B, float *C, int64_t M, int64_
   if (K == 0) return hip_status(q8::launch_empty_product(C, (int)M, (int)N, alpha, corr, stream));
   const bool wide = K % 4 == 0 && (trans_b || N % 4 == 0) && address_alignment(A) >= 16 &&
                     address_alignment(B) >= 16;
+  if (log_debug())
+    log_line("%s M=%lld K=%lld N=%lld: bf16 matrix cores (three-part split), %s%s", trans_b ? "dot_t_f32" : "dot_f32",
+             (long long)M, (long long)K, (long long)N, wide ? "16-byte loads" : "4-byte loads: ",
+             wide ? "" : K % 4 ? "K % 4 != 0" : (!trans_b && N % 4) ? "N % 4 != 0" : "A or B not 16-byte aligned");
   q8::DenseArgs a;
   a.A = A;
   a.B = B;
@@ -607,6 +670,19 @@ q8_status q8_dot_t(const int8_t *A, const int8_t *W, int32_t *C, int64_t M, int6
   q8_status st = current_device(&dev, &info);
   if (st != Q8_OK) return st;
   if (K == 0) return hip_status(q8::launch_zero_fill(C, (size_t)(M * N), stream));
+  if (log_debug()) {
+    const int path = q8::dot_t_path((int)M, (int)K, A, W);
+    const bool a16 = address_alignment(A) >= 16 && address_alignment(W) >= 16;
+    log_line("dot_t M=%lld K=%lld N=%lld: %s%s%s", (long long)M, (long long)K, (long long)N,
+             path == 2 ? "i8 matrix cores" : path == 1 ? "sdot4" : "scalar",
+             path == 2 ? "" : "; not on the matrix cores: ",
+             path == 2   ? ""
+             : M < 16    ? "M < 16 fills no 16-row tile"
+             : K % 16    ? "K % 16 != 0"
+             : !a16      ? "A or W not 16-byte aligned"
+                         : "");
+    if (path == 0) log_line("dot_t: no sdot4 either: %s", K % 4 ? "K % 4 != 0" : "A or W not 4-byte aligned");
+  }
   // The kernels put chunks of at most 32 rows of A on the grid's second
   // dimension: a taller A runs in slabs of rows, one launch each.
   constexpr int64_t kSlabRows = kMaxGridY / 2 * 32;  // a multiple of 32 rows

@@ -148,4 +148,7 @@ struct DotArgs {
 
 hipError_t launch_dot_t(const DotArgs &args, hipStream_t stream);
 
+// The dot_t kernel a call takes: 2 the i8 matrix cores, 1 sdot4, 0 scalar.
+int dot_t_path(int M, int K, const void *A, const void *W);
+
 }  // namespace q8

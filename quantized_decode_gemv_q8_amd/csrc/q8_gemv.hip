@@ -1,4 +1,8 @@
 // Host side of the Q8_0 matvec kernels: instance selection and launch.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "q8_gemv_kernel.h"
 
 namespace q8 {
@@ -16,6 +20,10 @@ __global__ void empty_product_kernel(float *C, int M, int N, float alpha, const 
     C[i] = y;
   }
 }
+
+// Dynamic LDS each (kernel instance, device) has opted in to.
+std::mutex g_lds_mu;
+std::map<std::pair<const void *, int>, size_t> g_lds_granted;
 
 GemvKernel pick(int vec, int m_tile) {
   switch (vec) {
@@ -39,12 +47,21 @@ hipError_t launch_gemv(int vec, int m_tile, const GemvArgs &args, int m_chunks, 
   if ((size_t)m_tile * count_max * kBlock > (size_t)64 * kStageRegs) return hipErrorInvalidValue;
   if (lds_bytes > kMaxGemvLds) return hipErrorInvalidValue;
   if (lds_bytes > 64 * 1024) {
-    // Above the default dynamic LDS limit the launch must opt in.
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
-      return e;
+    // Above the default dynamic LDS limit the launch must opt in, once per
+    // kernel instance and device, to the largest size it is launched with.
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_lds_mu);
+    size_t &granted = g_lds_granted[std::make_pair(reinterpret_cast<const void *>(k), dev)];
+    if (granted < lds_bytes) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds_bytes);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
+        return e;
+      }
+      granted = lds_bytes;
     }
   }
   hipLaunchKernelGGL(k, dim3((unsigned)args.n_wg, (unsigned)m_chunks, 1), dim3(kThreads), lds_bytes, stream, args);

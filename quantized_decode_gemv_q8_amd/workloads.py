@@ -70,6 +70,9 @@ WORKLOADS = {
     "mlp_gate_up_8192x28672": Workload("mlp_gate_up_8192x28672", "q8_fused", 1, 8192, 28672, "normal", "i8sym",
                                        (6, 0), siblings=2),
     "attn_qkv_4096": Workload("attn_qkv_4096", "q8_fused", 1, 4096, 4096, "normal", "i8sym", (7, 0), siblings=3),
+    # the fixed cost of one launch of the matvec kernel: 256 workgroups that
+    # each read a single 32-row block of 256 columns (M=1, K=32, N=65536)
+    "launch_floor_1x32x65536": Workload("launch_floor_1x32x65536", "q8", 1, 32, 65536, "normal", "i8sym", (12, 0)),
     # integer dot_t, weights stored one output row per row
     "dot_t_16x4096x4096": Workload("dot_t_16x4096x4096", "dot_t", 16, 4096, 4096, "i8full", "i8full", (5, 0)),
     # dense f32 product (square GEMM) and attention scores q @ k^T * 1/sqrt(128)
@@ -84,7 +87,8 @@ WORKLOADS = {
 # HBM.  Copy j draws from its own seed (``make(name, j)``).
 COPIES = {"tiny": 1, "attn4096": 57, "mlp_up_8192x28672": 4, "mlp_down_28672x8192": 4,
           "ragged_m4": 47, "dot_t_16x4096x4096": 63, "mlp_gate_up_8192x28672": 2, "attn_qkv_4096": 19,
-          "batch16_8192x28672": 4, "batch64_8192x28672": 4, "dot_f32_4096": 1, "scores_4096x4096_d128": 1}
+          "batch16_8192x28672": 4, "batch64_8192x28672": 4, "dot_f32_4096": 1, "scores_4096x4096_d128": 1,
+          "launch_floor_1x32x65536": 1}
 
 
 def _draw(rng, dist, shape):

@@ -225,3 +225,47 @@ def test_binding_checks_types_and_ranks_before_the_device():
         binding.q8_matvec(torch.zeros(4), torch.zeros((4, 1), dtype=torch.int8), torch.zeros((1, 1)))
     with pytest.raises(ValueError, match="rank 2"):
         binding.q8_dot_t_f32(torch.zeros((2, 2)), torch.zeros(2))
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+L = ctypes.CDLL(sys.argv[1])
+p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+for name, args in (
+        ("q8_matvec", [p, p, p, p, i64, i64, i64, p]),
+        ("q8_matvec_noalloc", [p, p, p, p, i64, i64, i64, p]),
+        ("q8_dot_t", [p, p, p, i64, i64, i64, p]),
+        ("q8_dot_f32", [p, p, p, i64, i64, i64, p, p]),
+        ("q8_dot_t_f32", [p, p, p, i64, i64, i64, p, p])):
+    getattr(L, name).argtypes = args
+    getattr(L, name).restype = ctypes.c_int
+L.q8_last_hip_error.restype = ctypes.c_int
+fake = [0x10000, 0x20000, 0x30000, 0x40000]
+out = [L.q8_matvec(*fake, 1, 256, 128, None), L.q8_matvec_noalloc(*fake, 4, 4100, 5000, None),
+       L.q8_dot_t(*fake[:3], 16, 4096, 4096, None), L.q8_dot_f32(*fake[:3], 130, 64, 200, None, None),
+       L.q8_dot_t_f32(*fake[:3], 130, 64, 200, None, None)]
+print(" ".join(str(x) for x in out), L.q8_last_hip_error())
+"""
+
+
+def test_valid_calls_without_a_device_return_an_error(tmp_path):
+    """With no GPU, valid calls (non-null pointers, in-range sizes) return an
+    error status from the first device query, before anything could touch the
+    pointers, and the process survives.  Run in a child process with every GPU
+    hidden, so that a crash cannot take the test runner down."""
+    import subprocess
+    import sys
+
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the fake pointers would be dereferenced")
+    script = tmp_path / "no_device.py"
+    script.write_text(_NO_DEVICE_SCRIPT)
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    res = subprocess.run([sys.executable, str(script), binding.LIB_PATH], capture_output=True, text=True,
+                         timeout=120, env=env)
+    assert res.returncode == 0, res.stderr
+    *statuses, hip_err = [int(x) for x in res.stdout.split()]
+    assert all(s in (binding.Q8_ERR_HIP, binding.Q8_ERR_UNSUPPORTED_DEVICE) for s in statuses), statuses
+    assert hip_err != 0
