@@ -545,6 +545,12 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
   a.rem = (int)L.rem;
   a.cmax = (int)L.cmax;
   a.pitch = q8::padded_pitch((int)L.count_max * kBlock, 4);
+  // Rows of W (N bytes) or S (4N bytes) that are not whole 128-byte lines
+  // share a line between neighbouring column tiles: with whole-tile runs, the
+  // workgroups take the runs in XCD bands so that each shared line is fetched
+  // into one L2 once (run_of_block).
+  const bool whole_runs = L.rem == 0 && L.upw > 0 && L.G % L.upw == 0 && L.n_tiles * (L.G / L.upw) == L.n_wg;
+  a.band_runs = (N % 128 != 0 && whole_runs) ? (int)(L.G / L.upw) : 0;
   const int64_t slab_chunks = L.m_chunks < kMaxGridY ? L.m_chunks : kMaxGridY;
   {
     Workspace ws;

@@ -23,6 +23,9 @@ __host__ __device__ constexpr int padded_pitch(int cols, int elem_bytes) {
   return (cols * elem_bytes) % kLdsBankPeriodBytes == 0 ? cols + 8 : cols;
 }
 
+// XCDs of the device: the dispatcher sends workgroup b of a grid to XCD b % kXcds.
+constexpr int kXcds = 8;
+
 // Weight sets sharing one activation matrix in a single launch.
 constexpr int kMaxSiblings = 4;
 
@@ -53,6 +56,7 @@ struct GemvArgs {
   int upw, rem;                   // units per workgroup
   int cmax;                       // most workgroups that share one tile
   int pitch;                      // row pitch of a wave's activation stage in LDS, floats
+  int band_runs;                  // > 0: runs per tile, workgroups take the runs in XCD bands (see run_of_block)
 };
 
 // Launches the Q8_0 matvec kernel instance (vec, m_tile) on `stream`.

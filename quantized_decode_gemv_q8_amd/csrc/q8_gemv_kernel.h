@@ -459,6 +459,22 @@ __device__ __forceinline__ int wg_of_unit(int u, int upw, int rem) {
   return u < big ? u / (upw + 1) : rem + (u - big) / upw;
 }
 
+// The run (in tile-major order) that workgroup b streams.  The dispatcher
+// sends workgroup b to XCD b % 8 (kXcds).  With band_runs > 0 (every tile cut
+// into band_runs runs, one per workgroup), the runs are taken K-range-major
+// and each XCD gets a contiguous stretch of that order: its workgroups read
+// neighbouring column tiles of the same rows together, so the 128-byte lines
+// that two tiles share when a row is not a multiple of 128 bytes are fetched
+// into one L2 once.  Which run a workgroup takes never changes a result.
+__device__ __forceinline__ int run_of_block(const GemvArgs &p, int b) {
+  if (p.band_runs <= 0) return b;
+  const int x = b % kXcds, k = b / kXcds;
+  const int q = p.n_wg / kXcds, rr = p.n_wg % kXcds;
+  const int i = x * q + min(x, rr) + k;
+  const int r = i / p.n_tiles, t = i - r * p.n_tiles;
+  return t * p.band_runs + r;
+}
+
 template <int VEC, int MT>
 __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
   using G = Geo<VEC>;
@@ -470,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = blockIdx.x;
+  const int wg = run_of_block(p, blockIdx.x);
   const int mc = blockIdx.y;
   const int m0 = mc * MT;
   const int u_begin = wg * p.upw + min(wg, p.rem);
