@@ -184,6 +184,12 @@ struct StaticSwitch {
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
+// Rows per pipelined chunk of instance (VEC, MT).  Instances wider than 16
+// columns x rows per lane use half-size chunks so that their register ring
+// of W fits beside the MT x VEC partial sums without spilling.
+template <int VEC, int MT>
+constexpr int kChunkRowsOf = VEC * MT > 16 ? Geo<VEC>::kChunkRows / 2 : Geo<VEC>::kChunkRows;
+
 // Per-wave streaming state.  A workgroup's run of units is one stream: wave w
 // takes block w of every group of the run, in order, so every wave of the
 // workgroup has `count` blocks.  The wave's k-th chunk (CR rows of one block)
@@ -196,8 +202,8 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 template <int VEC, int MT, int DEPTH>
 struct WaveStream {
   using G = Geo<VEC>;
-  static constexpr int CR = G::kChunkRows;
-  static constexpr int CPB = G::kChunksPerBlock;
+  static constexpr int CR = kChunkRowsOf<VEC, MT>;
+  static constexpr int CPB = kBlock / CR;
   static constexpr int NWD = G::kWords;
   static constexpr int TW = G::kTileCols;
   static constexpr int kDepth = DEPTH;  // register buffers (chunks) per wave
@@ -411,30 +417,32 @@ struct WaveStream {
 template <int VEC, int MT>
 constexpr int kStreamDepth = 4;
 
-// Writes output (row, n) of sibling `sib` through the epilogue of "dot and
-// tensor cores", section "The fused epilogue": the product x is updated per
-// element as it is written out, y = alpha * x + corr[row] * C[row, n] (the
-// second term only with row factors).  With alpha 1 and no row factors this
-// is a plain store of x.
-__device__ __forceinline__ void store_out(const GemvArgs &p, int sib, int row, int n, float x) {
-  float *c = p.C[sib] + (size_t)row * p.N + n;
-  float y = p.alpha * x;
-  if (p.corr != nullptr) y = fmaf(p.corr[row], *c, y);
-  *c = y;
-}
-
 // Stores outputs 4*o4 .. 4*o4+3 of row chunk m0's tile (sibling sib, tile
-// tis within the sibling), [MT][TW] in tile order, through the epilogue;
-// columns past N and rows past M are not stored.
+// tis within the sibling), [MT][TW] in tile order, through the epilogue of
+// "dot and tensor cores", section "The fused epilogue": each output x is
+// written as y = alpha * x + corr[row] * C[row, n] (the second term only with
+// row factors), so with alpha 1 and no row factors it is a plain store of x.
+// Columns past N and rows past M are not stored.  The arguments are read
+// once into registers: read per element, the compiler reloads them after
+// every store (it cannot rule out that a store changes them).
 template <int TW>
 __device__ __forceinline__ void store_quad(const GemvArgs &p, int sib, int tis, int m0, int o4, v4f x) {
+  float *const cs = p.C[sib];
+  const float alpha = p.alpha;
+  const float *const corr = p.corr;
+  const int N = p.N, M = p.M;
   const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int o = 4 * o4 + e;
     const int m = o / TW;
     const int n = tis * TW + (o - m * TW);
-    if (n < p.N && m0 + m < p.M) store_out(p, sib, m0 + m, n, xs[e]);
+    if (n < N && m0 + m < M) {
+      float *c = cs + (size_t)(m0 + m) * N + n;
+      float y = alpha * xs[e];
+      if (corr != nullptr) y = fmaf(corr[m0 + m], *c, y);
+      *c = y;
+    }
   }
 }
 
@@ -479,7 +487,7 @@ template <int VEC, int MT>
 __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
   using G = Geo<VEC>;
   constexpr int TW = G::kTileCols;
-  constexpr int CPB = G::kChunksPerBlock;
+  constexpr int CPB = kBlock / kChunkRowsOf<VEC, MT>;
 
   extern __shared__ __attribute__((aligned(16))) float lds[];
 
