@@ -417,49 +417,33 @@ struct WaveStream {
 template <int VEC, int MT>
 constexpr int kStreamDepth = 4;
 
-// Stores outputs 4*o4 .. 4*o4+3 of row chunk m0's tile (tile tis of the
-// sibling whose output is cs), [MT][TW] in tile order, through the epilogue
-// of "dot and tensor cores", section "The fused epilogue": each output x is
+// Stores outputs 4*o4 .. 4*o4+3 of row chunk m0's tile (sibling sib, tile
+// tis within the sibling), [MT][TW] in tile order, through the epilogue of
+// "dot and tensor cores", section "The fused epilogue": each output x is
 // written as y = alpha * x + corr[row] * C[row, n] (the second term only with
 // row factors), so with alpha 1 and no row factors it is a plain store of x.
-// Columns past N and rows past M are not stored.  A quad that lies whole
-// inside the row and is 16-byte aligned (N a multiple of 4, C aligned) goes
-// out as one 16-byte store.  The arguments come in as values: read through
-// the argument struct per element, the compiler reloads them after every
-// store (it cannot rule out that a store changes them).
+// Columns past N and rows past M are not stored.  The arguments are read
+// once into registers: read per element, the compiler reloads them after
+// every store (it cannot rule out that a store changes them).
 template <int TW>
-__device__ __forceinline__ void store_quad_to(float *cs, float alpha, const float *corr, int N, int M, int tis, int m0, int o4,
-                                              v4f x) {
-  // The quad lies in one row of the tile (TW is a multiple of 4).
-  const int o = 4 * o4;
-  const int m = o / TW;
-  const int n = tis * TW + (o - m * TW);
-  if (m0 + m >= M) return;
-  float *c = cs + (size_t)(m0 + m) * N + n;
-  const float rf = corr != nullptr ? corr[m0 + m] : 0.f;
-  if (n + 4 <= N && (N & 3) == 0 && ((uintptr_t)cs & 15) == 0) {
-    // The whole quad, 16-byte aligned: one load (with row factors) and one store.
-    v4f y = alpha * x;
-    if (corr != nullptr) {
-      const v4f old = *reinterpret_cast<const v4f *>(c);
-      y = v4f{fmaf(rf, old.x, y.x), fmaf(rf, old.y, y.y), fmaf(rf, old.z, y.z), fmaf(rf, old.w, y.w)};
-    }
-    *reinterpret_cast<v4f *>(c) = y;
-    return;
-  }
+__device__ __forceinline__ void store_quad(const GemvArgs &p, int sib, int tis, int m0, int o4, v4f x) {
+  float *const cs = p.C[sib];
+  const float alpha = p.alpha;
+  const float *const corr = p.corr;
+  const int N = p.N, M = p.M;
   const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if (n + e < N) {
+    const int o = 4 * o4 + e;
+    const int m = o / TW;
+    const int n = tis * TW + (o - m * TW);
+    if (n < N && m0 + m < M) {
+      float *c = cs + (size_t)(m0 + m) * N + n;
       float y = alpha * xs[e];
-      if (corr != nullptr) y = fmaf(rf, c[e], y);
-      c[e] = y;
+      if (corr != nullptr) y = fmaf(corr[m0 + m], *c, y);
+      *c = y;
     }
   }
-}
-template <int TW>
-__device__ __forceinline__ void store_quad(const GemvArgs &p, int sib, int tis, int m0, int o4, v4f x) {
-  store_quad_to<TW>(p.C[sib], p.alpha, p.corr, p.N, p.M, tis, m0, o4, x);
 }
 
 // Cache policy of the split-K partials' stores and loads: device-coherent
@@ -469,27 +453,11 @@ __device__ __forceinline__ void store_quad(const GemvArgs &p, int sib, int tis, 
 constexpr int kDeviceCoherent = 16;
 // Contributors summed by one pairwise tree in a split-K combine.
 constexpr int kCombineGroup = 8;
-// Four adjacent outputs of one contributor's slot: voff = 16 * o4 (the
-// thread's quad), soff = the slot's byte offset in the tile (uniform, so the
-// address costs no vector instruction).
-__device__ __forceinline__ v4f load_slot(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
-  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kDeviceCoherent);
+// Outputs 4*o4 .. 4*o4+3 of contributor c's partial (stride `per` floats).
+__device__ __forceinline__ v4f load_partial_quad(__amdgpu_buffer_rsrc_t rs, int c, int o4, int per) {
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, ((uint32_t)c * (uint32_t)per + 4u * (uint32_t)o4) * 4u, 0,
+                                                      kDeviceCoherent);
   return v4f{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
-}
-__device__ __forceinline__ void store_slot(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, v4f x) {
-  __builtin_amdgcn_raw_buffer_store_b128(v4u{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)},
-                                         rs, voff, soff, kDeviceCoherent);
-}
-
-// Sum of one group of contributors' partials, v[0..G) in K order (G = 4 or
-// 8; slots past the last contributor read as zero): the pairwise tree of the
-// split-K combine, plus the zero of the absent half of a group of eight and
-// of the cascade's empty levels, so that the result equals what SumCascade
-// returns for one group bit for bit (-0 comes out +0).
-template <int G>
-__device__ __forceinline__ v4f group_sum(const v4f (&v)[G]) {
-  if constexpr (G == 4) return ((v[0] + v[1]) + (v[2] + v[3])) + 0.f;
-  else return (((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]))) + 0.f;
 }
 
 // Workgroup that owns unit u when units are dealt in runs of upw (+1 for the
@@ -599,11 +567,10 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
   });
   lds_barrier();
 
-  // Finish every tile of the run, four adjacent outputs per thread: the four
-  // waves' sums, then a direct store (the run owns the whole tile) or a
+  // Finish every tile of the run: the four waves' sums, four adjacent outputs
+  // per thread, then a direct store (the run owns the whole tile) or a
   // published partial (one 16-byte device-coherent store per thread).
   constexpr int kQuads = MT * TW / 4;
-  constexpr uint32_t kSlotBytes = MT * TW * 4;
   bool any_partial = false;
   for (int q = 0; q < nseg; ++q) {
     const int t = t_first + q;
@@ -618,11 +585,12 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
       }
     } else {
       const __amdgpu_buffer_rsrc_t rs =
-          buffer_rsrc(p.partial + (size_t)(mc * p.n_tiles + t) * p.cmax * (MT * TW), (uint32_t)(i1 - i0 + 1) * kSlotBytes);
-      const uint32_t soff = (uint32_t)(wg - i0) * kSlotBytes;
+          buffer_rsrc(p.partial + ((size_t)(mc * p.n_tiles + t) * p.cmax + (wg - i0)) * (MT * TW), MT * TW * 4);
       for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
         const v4f x = (sl[o4] + sl[kQuads + o4]) + (sl[2 * kQuads + o4] + sl[3 * kQuads + o4]);
-        store_slot(rs, 16u * (uint32_t)o4, soff, x);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v4u{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)}, rs,
+            (uint32_t)o4 * 16u, 0, kDeviceCoherent);
       }
     }
   }
@@ -650,58 +618,61 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
     if (lane == 0) last_mask = (uint32_t)mask;
   }
   __syncthreads();
-  const uint32_t lm = last_mask;
-  if (lm == 0) return;
+  if (last_mask == 0) return;
   for (int q = 0; q < nseg; ++q) {
-    if (!(lm & (1u << q))) continue;
+    if (!(last_mask & (1u << q))) continue;
     const int t = t_first + q;
-    const int n = seg_hi[q] - seg_lo[q] + 1;  // contributors
-    // The partials are read with 16-byte device-coherent loads; the
-    // descriptor ends at the last contributor, so reads past it return zero.
-    // The summation order is the same for every instance: a pairwise tree
-    // over each group of eight contributors (absent ones are zero), then the
-    // group sums in K order through a cascade (SumCascade); up to eight
-    // contributors that is one tree (group_sum).
-    const __amdgpu_buffer_rsrc_t rs =
-        buffer_rsrc(p.partial + (size_t)(mc * p.n_tiles + t) * p.cmax * (MT * TW), (uint32_t)n * kSlotBytes);
+    const int i0 = seg_lo[q];
+    const int contributors = seg_hi[q] - i0 + 1;
+    // Each thread owns four adjacent outputs.  The summation order is the
+    // same for every instance: a pairwise tree over each group of eight
+    // contributors (absent ones are zero), then the group sums in K order
+    // through a cascade (SumCascade).  The partials are read with 16-byte
+    // device-coherent loads, two groups per round trip; the descriptor ends
+    // at the last contributor, so reads past it return zero.
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.partial + (size_t)(mc * p.n_tiles + t) * p.cmax * (MT * TW),
+                                                  (uint32_t)contributors * (MT * TW * 4));
     const int sib = t / p.tiles_per;
-    for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
-      const uint32_t voff = 16u * (uint32_t)o4;
-      v4f r;
-      if (n <= 4) {
-        v4f v[4];
+    if constexpr (VEC >= 8) {
+      // Up to four contributors (the large decode shapes at these widths):
+      // one pairwise tree, plus the zero of the absent half of the group of
+      // eight and of the cascade's empty levels, which is what the general
+      // path below returns for them, bit for bit (-0 comes out +0).  Only
+      // the wide instances carry this path; the narrow ones keep their code
+      // as it was, which measured faster for them.
+      if (contributors <= 4) {
+        for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
+          v4f v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = load_slot(rs, voff, i * kSlotBytes);
-        r = group_sum<4>(v);
-      } else if (n <= kCombineGroup) {
-        v4f v[kCombineGroup];
-#pragma unroll
-        for (int i = 0; i < kCombineGroup; ++i) v[i] = load_slot(rs, voff, i * kSlotBytes);
-        r = group_sum<kCombineGroup>(v);
-      } else {
-        SumCascade<float, 4> total;
-        for (int c = 0; c < n; c += 2 * kCombineGroup) {
-          v4f v[2 * kCombineGroup];
-#pragma unroll
-          for (int i = 0; i < kCombineGroup; ++i) v[i] = load_slot(rs, voff, (c + i) * kSlotBytes);
-          const bool second = n - c > kCombineGroup;
-          if (second) {
-#pragma unroll
-            for (int i = kCombineGroup; i < 2 * kCombineGroup; ++i) v[i] = load_slot(rs, voff, (c + i) * kSlotBytes);
-          }
-#pragma unroll
-          for (int g = 0; g < (second ? 2 : 1) * kCombineGroup; g += kCombineGroup) {
-            const v4f *y = &v[g];
-            const v4f s = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
-            const float xs[4] = {s.x, s.y, s.z, s.w};
-            total.add(xs);
-          }
+          for (int i = 0; i < 4; ++i) v[i] = load_partial_quad(rs, i, o4, MT * TW);
+          store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, ((v[0] + v[1]) + (v[2] + v[3])) + 0.f);
         }
-        float sum[4];
-        total.result(sum);
-        r = v4f{sum[0], sum[1], sum[2], sum[3]};
+        if (tid == 0) __hip_atomic_store(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        continue;
       }
-      store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, r);
+    }
+    for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
+      SumCascade<float, 4> total;
+      for (int c = 0; c < contributors; c += 2 * kCombineGroup) {
+        v4f v[2 * kCombineGroup];
+#pragma unroll
+        for (int i = 0; i < kCombineGroup; ++i) v[i] = load_partial_quad(rs, c + i, o4, MT * TW);
+        const bool second = contributors - c > kCombineGroup;
+        if (second) {
+#pragma unroll
+          for (int i = kCombineGroup; i < 2 * kCombineGroup; ++i) v[i] = load_partial_quad(rs, c + i, o4, MT * TW);
+        }
+#pragma unroll
+        for (int g = 0; g < (second ? 2 : 1) * kCombineGroup; g += kCombineGroup) {
+          const v4f *y = &v[g];
+          const v4f s = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
+          const float x[4] = {s.x, s.y, s.z, s.w};
+          total.add(x);
+        }
+      }
+      float sum[4];
+      total.result(sum);
+      store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, v4f{sum[0], sum[1], sum[2], sum[3]});
     }
     if (tid == 0) __hip_atomic_store(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
