@@ -289,6 +289,28 @@ def test_long_k_many_contributors(M, K, N, contributors):
     assert np.array_equal(gpu_q8(np.float32(0.25) * A, W, S, plan), np.float32(0.25) * C)
 
 
+@pytest.mark.parametrize("vec", [8, 16])
+@pytest.mark.parametrize("contributors", [2, 3, 4, 5, 8])
+def test_few_contributors(vec, contributors):
+    """Tiles shared by 2-8 workgroups at the wide lanes: up to four
+    contributors the last arrival adds the partials as one pairwise tree, more
+    go through the general combine.  Parity, zero columns come out +0 exactly,
+    repeated calls agree bitwise and a power-of-two scale of A scales C
+    exactly."""
+    M, K, N = 2, 4096, 2048
+    A, W, S = rand_q8(M, K, N, (141, vec, contributors))
+    S[:, 5] = 0  # a column whose every partial is zero
+    tiles = N // (64 * vec)
+    plan = {"vec": vec, "m_tile": 1, "workgroups": tiles * contributors, "kind": binding.PLAN_STREAM}
+    print(f"[q8] few contributors vec={vec} contributors={contributors}", flush=True)
+    C = gpu_q8(A, W, S, plan)
+    assert_parity(A, W, S, C)
+    assert np.all(C[:, 5].view(np.uint32) == 0)
+    assert np.array_equal(gpu_q8(A, W, S, plan).view(np.uint32), C.view(np.uint32))
+    C4 = gpu_q8(np.float32(4.0) * A, W, S, plan)
+    assert np.array_equal(C4.view(np.uint32), (np.float32(4.0) * C).view(np.uint32))
+
+
 def test_many_counters():
     # 8 row chunks x 128 column tiles: 1024 split-K counters, each on a line of
     # its own, far more than the smallest counter allocation
