@@ -58,6 +58,7 @@ constexpr int kTargetWgsPerCu = 1;
 struct DevInfo {
   bool gfx950;
   int cus;
+  int xcd_placement = -1;  // 1: verified round-robin placement of workgroups over XCDs, 0: not, -1: not checked yet
 };
 
 struct Workspace {
@@ -108,6 +109,60 @@ q8_status current_device(int *dev, DevInfo *info) {
   }
   *info = d;
   return d.gfx950 ? Q8_OK : Q8_ERR_UNSUPPORTED_DEVICE;
+}
+
+// XCD placement probe.  The split-K combine can keep a tile's partials in one
+// XCD's L2 when all of the tile's runs go to workgroups b with the same
+// b % 8, on the premise that the dispatcher places those on one XCD (it deals
+// workgroups to the XCDs in turn).  Before the first such launch on a device,
+// a probe kernel records the XCD of each of kProbeWgs workgroups in two
+// launches of different sizes; the premise holds if every workgroup's XCD
+// depends only on b % 8.  The kernel also checks the placement of every
+// tile's contributors as it counts them, and writes NaN rather than a wrong
+// sum if a tile's contributors ran on different XCDs.
+constexpr int kProbeWgs = 4096;
+static __device__ uint32_t xcc_probe_out[kProbeWgs];
+
+bool probe_placement(hipStream_t stream) {
+  uint32_t *out = nullptr;
+  if (hipGetSymbolAddress((void **)&out, HIP_SYMBOL(xcc_probe_out)) != hipSuccess) return false;
+  std::vector<uint32_t> host(kProbeWgs);
+  for (int n : {kProbeWgs, kProbeWgs - 3}) {
+    if (q8::launch_xcc_probe(out, n, stream) != hipSuccess) return false;
+    if (hipStreamSynchronize(stream) != hipSuccess) return false;
+    if (hipMemcpy(host.data(), out, (size_t)n * sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return false;
+    for (int b = 0; b < n; ++b)
+      if (host[b] >= (uint32_t)q8::kXcds || host[b] != host[b % q8::kXcds]) return false;
+  }
+  return true;
+}
+
+// Whether the XCD-local combine may be used on device `dev`: probes once
+// (not while `stream` is being captured, when a synchronising probe cannot
+// run; such a call uses the device-coherent combine).
+bool xcd_placement_ok(int dev, hipStream_t stream) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_dev.find(dev);
+    if (it != g_dev.end() && it->second.xcd_placement >= 0) return it->second.xcd_placement == 1;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+  const bool ok = probe_placement(stream);
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_dev[dev].xcd_placement = ok ? 1 : 0;
+  return ok;
+}
+
+// Q8_XCD_LOCAL=0 turns the XCD-local combine off; Q8_XCD_LOCAL=stray makes
+// some contributors of every tile report another XCD, which the kernel must
+// turn into NaN outputs (used to test that check).
+int xcd_local_mode() {
+  const char *v = getenv("Q8_XCD_LOCAL");
+  if (v == nullptr) return 1;
+  if (strcmp(v, "0") == 0) return 0;
+  if (strcmp(v, "stray") == 0) return 2;
+  return 1;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -551,6 +606,21 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
   // into one L2 once (run_of_block).
   const bool whole_runs = L.rem == 0 && L.upw > 0 && L.G % L.upw == 0 && L.n_tiles * (L.G / L.upw) == L.n_wg;
   a.band_runs = (N % 128 != 0 && whole_runs) ? (int)(L.G / L.upw) : 0;
+  // Otherwise, with whole-tile runs and a multiple of 8 tiles and
+  // workgroups, each tile's runs go to one XCD and its partials stay in that
+  // XCD's L2 (at most 63 runs per tile: the counter's per-XCD fields).
+  const int64_t runs = whole_runs ? L.G / L.upw : 0;
+  const int xmode = xcd_local_mode();
+  a.xcd_runs = 0;
+  a.xcc_skew = 0;
+  if (a.band_runs == 0 && whole_runs && runs >= 2 && runs <= 63 && L.n_wg % q8::kXcds == 0 &&
+      L.n_tiles % q8::kXcds == 0 && xmode != 0 && xcd_placement_ok(dev, stream)) {
+    a.xcd_runs = (int)runs;
+    a.xcc_skew = xmode == 2 ? 1 : 0;
+  }
+  if (log_debug() && a.xcd_runs > 0)
+    log_line("%s: split-K partials kept in the XCD L2 (%lld tiles of %lld runs, each tile on one XCD)",
+             no_alloc ? "matvec_noalloc" : "matvec", (long long)L.n_tiles, (long long)runs);
   const int64_t slab_chunks = L.m_chunks < kMaxGridY ? L.m_chunks : kMaxGridY;
   {
     Workspace ws;

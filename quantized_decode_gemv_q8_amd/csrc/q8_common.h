@@ -57,12 +57,18 @@ struct GemvArgs {
   int cmax;                       // most workgroups that share one tile
   int pitch;                      // row pitch of a wave's activation stage in LDS, floats
   int band_runs;                  // > 0: runs per tile, workgroups take the runs in XCD bands (see run_of_block)
+  int xcd_runs;                   // > 0: runs per tile, all runs of a tile on one XCD; the split-K
+                                  //      partials then stay in that XCD's L2 (see run_of_block)
+  int xcc_skew;                   // testing only: nonzero makes some contributors report another XCD
 };
 
 // Launches the Q8_0 matvec kernel instance (vec, m_tile) on `stream`.
 // Returns hipErrorInvalidValue for an instance that is not compiled.
 hipError_t launch_gemv(int vec, int m_tile, const GemvArgs &args, int m_chunks,
                        size_t lds_bytes, hipStream_t stream);
+
+// Writes, for each of n_wg workgroups, the id of the XCD it ran on to out[b].
+hipError_t launch_xcc_probe(uint32_t *out, int n_wg, hipStream_t stream);
 
 // Writes `n` zero words at `p` (used for fresh counters).
 hipError_t launch_zero_fill(void *p, size_t n_words, hipStream_t stream);

@@ -12,6 +12,14 @@ __global__ void zero_fill_kernel(uint32_t *p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
 
+// Records the XCD each workgroup runs on (the XCC_ID hardware register, low
+// four bits); written with a vector store by lane 0.
+__global__ void xcc_probe_kernel(uint32_t *out) {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  if (threadIdx.x == 0) out[blockIdx.x] = x & 15u;
+}
+
 __global__ void empty_product_kernel(float *C, int M, int N, float alpha, const float *corr) {
   const size_t total = (size_t)M * N;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
@@ -74,6 +82,12 @@ hipError_t launch_empty_product(float *C, int M, int N, float alpha, const float
   size_t blocks = (total + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(empty_product_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, M, N, alpha, corr);
+  return hipGetLastError();
+}
+
+hipError_t launch_xcc_probe(uint32_t *out, int n_wg, hipStream_t stream) {
+  if (n_wg < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(xcc_probe_kernel, dim3((unsigned)n_wg), dim3(64), 0, stream, out);
   return hipGetLastError();
 }
 

@@ -451,13 +451,35 @@ __device__ __forceinline__ void store_quad(const GemvArgs &p, int sib, int tis, 
 // once it is performed at the device's coherence point; a load misses in the
 // per-XCD caches and reads that point.
 constexpr int kDeviceCoherent = 16;
+// When all contributors of a tile run on one XCD: stores with the default
+// policy (acknowledged once they are in the XCD's L2) and loads with sc0
+// (they miss in the CU's L1 and read the L2).
+constexpr int kXcdStore = 0;
+constexpr int kXcdLoad = 1;
 // Contributors summed by one pairwise tree in a split-K combine.
 constexpr int kCombineGroup = 8;
 // Outputs 4*o4 .. 4*o4+3 of contributor c's partial (stride `per` floats).
+template <int AUX>
 __device__ __forceinline__ v4f load_partial_quad(__amdgpu_buffer_rsrc_t rs, int c, int o4, int per) {
-  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, ((uint32_t)c * (uint32_t)per + 4u * (uint32_t)o4) * 4u, 0,
-                                                      kDeviceCoherent);
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, ((uint32_t)c * (uint32_t)per + 4u * (uint32_t)o4) * 4u, 0, AUX);
   return v4f{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+}
+
+// Id of the XCD this wave runs on (the XCC_ID hardware register; its low
+// four bits).
+__device__ __forceinline__ uint32_t xcd_id() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 15u;
+}
+
+// The split-K counter of a tile whose runs are placed on one XCD is 64 bits:
+// the number of contributors in bits 0-14, a count of contributors that
+// report an XCD numbered 8 or above from bit 15, and a 6-bit count per XCD x
+// at bit 16 + 6x.  A contributor on XCD x adds xcd_increment(x); the last one
+// checks that every contributor counted on its own XCD.
+__device__ __forceinline__ uint64_t xcd_increment(uint32_t x) {
+  return 1ull + (x < 8 ? 1ull << (16 + 6 * x) : 1ull << 15);
 }
 
 // Workgroup that owns unit u when units are dealt in runs of upw (+1 for the
@@ -474,13 +496,104 @@ __device__ __forceinline__ int wg_of_unit(int u, int upw, int rem) {
 // neighbouring column tiles of the same rows together, so the 128-byte lines
 // that two tiles share when a row is not a multiple of 128 bytes are fetched
 // into one L2 once.  Which run a workgroup takes never changes a result.
+//
+// With xcd_runs > 0 (every tile cut into xcd_runs runs, and the number of
+// tiles a multiple of 8), all runs of tile t go to the workgroups b with
+// b % 8 == t % 8, which the dispatcher places on one XCD: a tile's partials
+// are then written and read in that XCD's L2.
 __device__ __forceinline__ int run_of_block(const GemvArgs &p, int b) {
+  if (p.xcd_runs > 0) {
+    const int R = p.xcd_runs, x = b % kXcds, k = b / kXcds;
+    return (kXcds * (k / R) + x) * R + k % R;
+  }
   if (p.band_runs <= 0) return b;
   const int x = b % kXcds, k = b / kXcds;
   const int q = p.n_wg / kXcds, rr = p.n_wg % kXcds;
   const int i = x * q + min(x, rr) + k;
   const int r = i / p.n_tiles, t = i - r * p.n_tiles;
   return t * p.band_runs + r;
+}
+
+// The combine of the tiles this workgroup completed (bit q of last_mask:
+// segment q), reading the partials with cache policy AUX.  A tile in
+// stray_mask gets NaN outputs.  Re-arms the counters.
+template <int VEC, int MT, int AUX>
+__device__ __forceinline__ void combine_tiles(const GemvArgs &p, uint32_t last_mask, uint32_t stray_mask, const int *seg_lo,
+                                              const int *seg_hi, int nseg, int t_first, int mc, int m0, int tid) {
+  using G = Geo<VEC>;
+  constexpr int TW = G::kTileCols;
+  constexpr int kQuads = MT * TW / 4;
+  auto rearm = [&](int t) {
+    if (tid != 0) return;
+    uint32_t *cnt = &p.counters[(mc * p.n_tiles + t) * kCounterStride];
+    if constexpr (AUX == kXcdLoad)
+      __hip_atomic_store(reinterpret_cast<uint64_t *>(cnt), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int q = 0; q < nseg; ++q) {
+    if (!(last_mask & (1u << q))) continue;
+    const int t = t_first + q;
+    const int i0 = seg_lo[q];
+    const int contributors = seg_hi[q] - i0 + 1;
+    const int sib = t / p.tiles_per;
+    if (stray_mask & (1u << q)) {
+      const float nan = __builtin_nanf("");
+      for (int o4 = tid; o4 < kQuads; o4 += kThreads) store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, v4f{nan, nan, nan, nan});
+      rearm(t);
+      continue;
+    }
+    // Each thread owns four adjacent outputs.  The summation order is the
+    // same for every instance: a pairwise tree over each group of eight
+    // contributors (absent ones are zero), then the group sums in K order
+    // through a cascade (SumCascade).  The partials are read with 16-byte
+    // device-coherent loads, two groups per round trip; the descriptor ends
+    // at the last contributor, so reads past it return zero.
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.partial + (size_t)(mc * p.n_tiles + t) * p.cmax * (MT * TW),
+                                                  (uint32_t)contributors * (MT * TW * 4));
+    if constexpr (VEC >= 8) {
+      // Up to four contributors (the large decode shapes at these widths):
+      // one pairwise tree, plus the zero of the absent half of the group of
+      // eight and of the cascade's empty levels, which is what the general
+      // path below returns for them, bit for bit (-0 comes out +0).  Only
+      // the wide instances carry this path; the narrow ones keep their code
+      // as it was, which measured faster for them.
+      if (contributors <= 4) {
+        for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
+          v4f v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = load_partial_quad<AUX>(rs, i, o4, MT * TW);
+          store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, ((v[0] + v[1]) + (v[2] + v[3])) + 0.f);
+        }
+        rearm(t);
+        continue;
+      }
+    }
+    for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
+      SumCascade<float, 4> total;
+      for (int c = 0; c < contributors; c += 2 * kCombineGroup) {
+        v4f v[2 * kCombineGroup];
+#pragma unroll
+        for (int i = 0; i < kCombineGroup; ++i) v[i] = load_partial_quad<AUX>(rs, c + i, o4, MT * TW);
+        const bool second = contributors - c > kCombineGroup;
+        if (second) {
+#pragma unroll
+          for (int i = kCombineGroup; i < 2 * kCombineGroup; ++i) v[i] = load_partial_quad<AUX>(rs, c + i, o4, MT * TW);
+        }
+#pragma unroll
+        for (int g = 0; g < (second ? 2 : 1) * kCombineGroup; g += kCombineGroup) {
+          const v4f *y = &v[g];
+          const v4f s = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
+          const float x[4] = {s.x, s.y, s.z, s.w};
+          total.add(x);
+        }
+      }
+      float sum[4];
+      total.result(sum);
+      store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, v4f{sum[0], sum[1], sum[2], sum[3]});
+    }
+    rearm(t);
+  }
 }
 
 template <int VEC, int MT>
@@ -569,8 +682,10 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
 
   // Finish every tile of the run: the four waves' sums, four adjacent outputs
   // per thread, then a direct store (the run owns the whole tile) or a
-  // published partial (one 16-byte device-coherent store per thread).
+  // published partial (one 16-byte store per thread: device-coherent, or
+  // into the XCD's L2 when the tile's runs are all on this XCD).
   constexpr int kQuads = MT * TW / 4;
+  const bool local = p.xcd_runs > 0;
   bool any_partial = false;
   for (int q = 0; q < nseg; ++q) {
     const int t = t_first + q;
@@ -588,94 +703,62 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
           buffer_rsrc(p.partial + ((size_t)(mc * p.n_tiles + t) * p.cmax + (wg - i0)) * (MT * TW), MT * TW * 4);
       for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
         const v4f x = (sl[o4] + sl[kQuads + o4]) + (sl[2 * kQuads + o4] + sl[3 * kQuads + o4]);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            v4u{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)}, rs,
-            (uint32_t)o4 * 16u, 0, kDeviceCoherent);
+        const v4u u = v4u{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)};
+        if (local)
+          __builtin_amdgcn_raw_buffer_store_b128(u, rs, (uint32_t)o4 * 16u, 0, kXcdStore);
+        else
+          __builtin_amdgcn_raw_buffer_store_b128(u, rs, (uint32_t)o4 * 16u, 0, kDeviceCoherent);
       }
     }
   }
   if (!any_partial) return;
 
   // Count each shared tile's contribution once this workgroup's partials are
-  // performed at device scope (s_waitcnt: the coherent stores are
-  // acknowledged only when they have reached the device's coherence point):
-  // lane q of wave 0 bumps segment q's counter, all in one go.  The last of a
-  // tile's contributors combines it.
+  // performed where the reader will look (s_waitcnt: device-coherent stores
+  // are acknowledged only once they have reached the device's coherence
+  // point, the others once they are in the XCD's L2): lane q of wave 0 bumps
+  // segment q's counter, all in one go.  The last of a tile's contributors
+  // combines it.  With the tile's runs on one XCD the counter also records
+  // where each contributor ran; a tile with a contributor on another XCD (the
+  // dispatcher did not place the workgroups as expected) cannot be read from
+  // this L2, and its outputs are written as NaN instead of a wrong sum.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  __shared__ uint32_t stray_mask;
   if (wave == 0) {
-    bool last = false;
+    bool last = false, stray = false;
     if (lane < nseg) {
       const int t = t_first + lane;
       const int i0 = seg_lo[lane], i1 = seg_hi[lane];
       if (i0 != i1) {
-        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        last = prev == (uint32_t)(i1 - i0);
+        uint32_t *cnt = &p.counters[(mc * p.n_tiles + t) * kCounterStride];
+        if (local) {
+          const uint32_t x = xcd_id() ^ (p.xcc_skew != 0 ? (uint32_t)(blockIdx.x / kXcds) & 1u : 0u);
+          const uint64_t inc = xcd_increment(x);
+          const uint64_t prev = __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(cnt), inc, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t n = (uint64_t)(i1 - i0 + 1);
+          last = (prev & 0x7fffu) == n - 1;
+          stray = last && (x >= 8 || prev + inc != n + (n << (16 + 6 * x)));
+        } else {
+          const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          last = prev == (uint32_t)(i1 - i0);
+        }
       }
     }
     const uint64_t mask = __ballot(last);
-    if (lane == 0) last_mask = (uint32_t)mask;
+    const uint64_t smask = __ballot(stray);
+    if (lane == 0) {
+      last_mask = (uint32_t)mask;
+      stray_mask = (uint32_t)smask;
+    }
   }
   __syncthreads();
   if (last_mask == 0) return;
-  for (int q = 0; q < nseg; ++q) {
-    if (!(last_mask & (1u << q))) continue;
-    const int t = t_first + q;
-    const int i0 = seg_lo[q];
-    const int contributors = seg_hi[q] - i0 + 1;
-    // Each thread owns four adjacent outputs.  The summation order is the
-    // same for every instance: a pairwise tree over each group of eight
-    // contributors (absent ones are zero), then the group sums in K order
-    // through a cascade (SumCascade).  The partials are read with 16-byte
-    // device-coherent loads, two groups per round trip; the descriptor ends
-    // at the last contributor, so reads past it return zero.
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.partial + (size_t)(mc * p.n_tiles + t) * p.cmax * (MT * TW),
-                                                  (uint32_t)contributors * (MT * TW * 4));
-    const int sib = t / p.tiles_per;
-    if constexpr (VEC >= 8) {
-      // Up to four contributors (the large decode shapes at these widths):
-      // one pairwise tree, plus the zero of the absent half of the group of
-      // eight and of the cascade's empty levels, which is what the general
-      // path below returns for them, bit for bit (-0 comes out +0).  Only
-      // the wide instances carry this path; the narrow ones keep their code
-      // as it was, which measured faster for them.
-      if (contributors <= 4) {
-        for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
-          v4f v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = load_partial_quad(rs, i, o4, MT * TW);
-          store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, ((v[0] + v[1]) + (v[2] + v[3])) + 0.f);
-        }
-        if (tid == 0) __hip_atomic_store(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        continue;
-      }
-    }
-    for (int o4 = tid; o4 < kQuads; o4 += kThreads) {
-      SumCascade<float, 4> total;
-      for (int c = 0; c < contributors; c += 2 * kCombineGroup) {
-        v4f v[2 * kCombineGroup];
-#pragma unroll
-        for (int i = 0; i < kCombineGroup; ++i) v[i] = load_partial_quad(rs, c + i, o4, MT * TW);
-        const bool second = contributors - c > kCombineGroup;
-        if (second) {
-#pragma unroll
-          for (int i = kCombineGroup; i < 2 * kCombineGroup; ++i) v[i] = load_partial_quad(rs, c + i, o4, MT * TW);
-        }
-#pragma unroll
-        for (int g = 0; g < (second ? 2 : 1) * kCombineGroup; g += kCombineGroup) {
-          const v4f *y = &v[g];
-          const v4f s = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
-          const float x[4] = {s.x, s.y, s.z, s.w};
-          total.add(x);
-        }
-      }
-      float sum[4];
-      total.result(sum);
-      store_quad<TW>(p, sib, t - sib * p.tiles_per, m0, o4, v4f{sum[0], sum[1], sum[2], sum[3]});
-    }
-    if (tid == 0) __hip_atomic_store(&p.counters[(mc * p.n_tiles + t) * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (local)
+    combine_tiles<VEC, MT, kXcdLoad>(p, last_mask, stray_mask, seg_lo, seg_hi, nseg, t_first, mc, m0, tid);
+  else
+    combine_tiles<VEC, MT, kDeviceCoherent>(p, last_mask, stray_mask, seg_lo, seg_hi, nseg, t_first, mc, m0, tid);
 }
 
 typedef void (*GemvKernel)(GemvArgs);

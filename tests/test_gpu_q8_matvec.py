@@ -5,6 +5,7 @@ Bar: max over outputs of |C_gpu - C_oracle| / D <= 1e-5, where D is the sum of
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -309,6 +310,52 @@ def test_few_contributors(vec, contributors):
     assert np.array_equal(gpu_q8(A, W, S, plan).view(np.uint32), C.view(np.uint32))
     C4 = gpu_q8(np.float32(4.0) * A, W, S, plan)
     assert np.array_equal(C4.view(np.uint32), (np.float32(4.0) * C).view(np.uint32))
+
+
+def _with_xcd_mode(mode, fn):
+    old = os.environ.get("Q8_XCD_LOCAL")
+    if mode is None:
+        os.environ.pop("Q8_XCD_LOCAL", None)
+    else:
+        os.environ["Q8_XCD_LOCAL"] = mode
+    try:
+        return fn()
+    finally:
+        if old is None:
+            os.environ.pop("Q8_XCD_LOCAL", None)
+        else:
+            os.environ["Q8_XCD_LOCAL"] = old
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2, 8192, 8192), (1, 28672, 4096)])
+def test_xcd_local_combine_is_bitwise_the_same(M, K, N, capfd):
+    """Tiles whose runs all sit on one XCD keep their split-K partials in that
+    XCD's L2; the sums are the same bit for bit as with device-coherent
+    partials (same partials, same order)."""
+    A, W, S = rand_q8(M, K, N, (142, M, K, N))
+    os.environ["Q8_LOG"] = "debug"
+    try:
+        C_local = _with_xcd_mode(None, lambda: gpu_q8(A, W, S))
+        C_dev = _with_xcd_mode("0", lambda: gpu_q8(A, W, S))
+    finally:
+        os.environ.pop("Q8_LOG", None)
+    err = capfd.readouterr().err
+    print(f"[q8] xcd-local M={M} K={K} N={N}", flush=True)
+    assert "kept in the XCD L2" in err, err
+    assert_parity(A, W, S, C_local)
+    assert np.array_equal(C_local.view(np.uint32), C_dev.view(np.uint32))
+
+
+def test_xcd_local_stray_contributors_give_nan():
+    """If a tile's contributors report different XCDs, the tile's outputs are
+    NaN (its partials may not be readable from one L2); the counters are
+    re-armed, so the next call is correct."""
+    M, K, N = 1, 4096, 4096
+    A, W, S = rand_q8(M, K, N, 143)
+    print("[q8] xcd-local stray contributors", flush=True)
+    C = _with_xcd_mode("stray", lambda: gpu_q8(A, W, S))
+    assert np.all(np.isnan(C))
+    assert_parity(A, W, S, gpu_q8(A, W, S))
 
 
 def test_many_counters():
