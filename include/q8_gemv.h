@@ -40,6 +40,18 @@
  *     eager call of the same (or a larger) shape on that stream first.
  *     Captured calls replay correctly: their arrival counters return to zero
  *     inside every launch, and no call records a memset.
+ *   - XCD placement: when a matvec plan cuts every column tile into whole
+ *     K runs and the tiles and workgroups are multiples of 8, the library
+ *     places all runs of a tile on one XCD (the dispatcher deals workgroups
+ *     to the eight XCDs in turn) and keeps the tile's split-K partials in
+ *     that XCD's L2.  The first such call on a device, unless its stream is
+ *     being captured, first runs a small probe kernel on the stream and
+ *     waits for it (once per device and process) to confirm that placement;
+ *     without it the partials go through the device's coherence point as for
+ *     other plans.  If the contributors of a tile are ever found on
+ *     different XCDs, that tile's outputs are written as NaN, never as a
+ *     wrong sum.  The environment variable Q8_XCD_LOCAL=0 turns this off;
+ *     results are bitwise the same either way.
  */
 #ifndef Q8_GEMV_H
 #define Q8_GEMV_H
