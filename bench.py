@@ -49,9 +49,11 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix peak
 DENSE_BF16_PRODUCTS = 6
 CSRC = os.path.join(ROOT, "quantized_decode_gemv_q8_amd", "csrc")
 # Sources whose hash stamps a traffic measurement (the kernel code itself).
-KERNEL_SRC = (os.path.join(CSRC, "q8_gemv_kernel.h"), os.path.join(CSRC, "q8_sum.h"), os.path.join(CSRC, "q8_common.h"))
+KERNEL_SRC = (os.path.join(CSRC, "q8_gemv_kernel.h"), os.path.join(CSRC, "q8_sum.h"), os.path.join(CSRC, "q8_xcd.h"),
+              os.path.join(CSRC, "q8_common.h"))
 DOT_SRC = (os.path.join(CSRC, "dot_t.hip"), os.path.join(CSRC, "q8_common.h"))
-GEMM_SRC = (os.path.join(CSRC, "q8_gemm.hip"), os.path.join(CSRC, "q8_sum.h"), os.path.join(CSRC, "q8_common.h"))
+GEMM_SRC = (os.path.join(CSRC, "q8_gemm.hip"), os.path.join(CSRC, "q8_sum.h"), os.path.join(CSRC, "q8_xcd.h"),
+            os.path.join(CSRC, "q8_common.h"))
 DENSE_SRC = (os.path.join(CSRC, "dense_f32.hip"), os.path.join(CSRC, "q8_common.h"))
 # Kernel-name prefix of each source set, as rocprofv3 reports it.
 KERNEL_NAMES = {KERNEL_SRC: "q8_gemv_kernel", GEMM_SRC: "q8_gemm_kernel", DOT_SRC: "dot_t_",

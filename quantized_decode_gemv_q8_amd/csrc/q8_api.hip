@@ -565,6 +565,19 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
     g.n_tiles = (int)ceil_div(N, q8::kGemmTileCols);
     g.splits = pl.workgroups / g.n_tiles;
     g.bps = (int)ceil_div(KB, g.splits);
+    // The splits of a tile are on grid y: with a multiple of 8 tiles they all
+    // run on the tile's XCD, and their partials can stay in its L2 (at most
+    // 63 splits: the counter's per-XCD fields).
+    const int xmode = xcd_local_mode();
+    g.xcd_local = 0;
+    g.xcc_skew = 0;
+    if (g.splits >= 2 && g.splits <= 63 && g.n_tiles % q8::kXcds == 0 && xmode != 0 && xcd_placement_ok(dev, stream)) {
+      g.xcd_local = 1;
+      g.xcc_skew = xmode == 2 ? 1 : 0;
+      if (log_debug())
+        log_line("%s: split-K partials kept in the XCD L2 (%d tiles of %d splits, each tile on one XCD)",
+                 no_alloc ? "matvec_noalloc" : "matvec", g.n_tiles, g.splits);
+    }
     Workspace ws;
     // Partials and counters per pass of 16 * gemm_row_tiles(M) rows.
     const int64_t rows = 16 * q8::gemm_row_tiles(M);

@@ -121,6 +121,8 @@ struct GemmArgs {
   uint32_t *counters;  // [passes][n_tiles] arrival counters (kCounterStride apart), zero between calls
   int M, K, N, KB;
   int n_tiles, splits, bps;
+  int xcd_local;       // nonzero: every split of a tile runs on one XCD (n_tiles a multiple of 8); partials stay in its L2
+  int xcc_skew;        // testing only: nonzero makes some splits report another XCD
 };
 
 // Rows of A the matrix-core product takes at most, its column tile and its

@@ -42,6 +42,7 @@
 
 #include "q8_common.h"
 #include "q8_sum.h"
+#include "q8_xcd.h"
 
 namespace q8 {
 namespace {
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   // barrier per block suffices.
   __shared__ __attribute__((aligned(16))) int8_t w_lds_buf[2][kBlock * kWPitch];
   __shared__ __attribute__((aligned(16))) uint16_t a_lds_buf[2][3][16 * RT * kAPitch];
-  __shared__ uint32_t last_flag;
+  __shared__ uint32_t last_flag, stray_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -340,8 +341,16 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   // The partial keeps the lanes' register layout: piece ((w*8 + t)*RT + r)*64
   // + l holds lane l's four values of tile (t, r) of wave w, so each store
   // instruction of a wave writes 1 KB contiguously.
+  // With xcd_local every split of this tile runs on this XCD (the tile is
+  // blockIdx.x, the split blockIdx.y, and the number of tiles is a multiple
+  // of 8, so the dispatcher's turn-by-turn placement puts them together): the
+  // partials are then stored into the XCD's L2 (acknowledged there) and read
+  // back from it with sc0, and the counter records each split's XCD; if a
+  // split ran elsewhere the tile's outputs are written as NaN.
   constexpr int kPieces = kTileElems / 4;
   constexpr int kCoherent = 16;  // cache policy: sc1, written through to the device's coherence point
+  constexpr int kL2Load = 1;     // sc0: past the CU's L1, from the XCD's L2
+  const bool local = p.xcd_local != 0;
   const __amdgpu_buffer_rsrc_t part_rs =
       rsrc(p.partial + (size_t)tile * p.splits * kTileElems, (uint32_t)p.splits * kTileElems * 4u);
 #pragma unroll
@@ -349,17 +358,54 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       const uint32_t piece = (uint32_t)(((wave * kWaveTiles + t) * RT + r) * 64 + lane);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, acc[t][r]), part_rs,
-                                             ((uint32_t)split * kPieces + piece) * 16u, 0u, kCoherent);
+      const u4 v = __builtin_bit_cast(u4, acc[t][r]);
+      const uint32_t off = ((uint32_t)split * kPieces + piece) * 16u;
+      if (local)
+        __builtin_amdgcn_raw_buffer_store_b128(v, part_rs, off, 0u, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b128(v, part_rs, off, 0u, kCoherent);
     }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  uint32_t *cnt = &p.counters[tile * kCounterStride];
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&p.counters[tile * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = prev == (uint32_t)(p.splits - 1);
+    if (local) {
+      const uint32_t x = xcd_id() ^ (p.xcc_skew != 0 ? (uint32_t)split & 1u : 0u);
+      const uint64_t prev = __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(cnt), xcd_increment(x), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = xcd_count_done(prev, (uint64_t)p.splits);
+      last_flag = last;
+      stray_flag = last && !xcd_all_here(prev, x, (uint64_t)p.splits);
+    } else {
+      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = prev == (uint32_t)(p.splits - 1);
+      stray_flag = 0;
+    }
   }
   __syncthreads();
   if (!last_flag) return;
+  auto rearm = [&]() {
+    if (tid != 0) return;
+    if (local)
+      __hip_atomic_store(reinterpret_cast<uint64_t *>(cnt), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (stray_flag) {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int t = 0; t < kWaveTiles; ++t)
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int m, col;
+          out_index(t, r, e, m, col);
+          if (m < p.M && n0 + col < p.N) p.C[(size_t)m * p.N + n0 + col] = nan;
+        }
+    rearm();
+    return;
+  }
   // Sum the splits in K order: pairwise over groups of eight, then the groups
   // in order through the cascade of the matvec's combine (SumCascade).
   // Thread (wave, lane) sums the pieces of its own accumulator tiles, BATCH
@@ -372,8 +418,8 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   // full cascade one piece at a time, within the 16-row instance's registers.
   const __amdgpu_buffer_rsrc_t none_rs = rsrc(p.partial, 0u);
   constexpr int kOwn = kWaveTiles * RT;  // pieces per thread
-  auto combine = [&](auto batch_, auto levels_) {
-    constexpr int BATCH = decltype(batch_)::value, LEVELS = decltype(levels_)::value;
+  auto combine = [&](auto batch_, auto levels_, auto aux_) {
+    constexpr int BATCH = decltype(batch_)::value, LEVELS = decltype(levels_)::value, AUX = decltype(aux_)::value;
     static_assert(kOwn % BATCH == 0, "whole batches of pieces");
 #pragma unroll
     for (int j0 = 0; j0 < kOwn; j0 += BATCH) {
@@ -390,7 +436,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
             const bool remote = sj < p.splits && sj != split;
             const uint32_t off = ((uint32_t)min(sj, p.splits - 1) * kPieces + piece) * 16u;
             const f4 x = __builtin_bit_cast(
-                f4, __builtin_amdgcn_raw_buffer_load_b128(remote ? part_rs : none_rs, off, 0u, kCoherent));
+                f4, __builtin_amdgcn_raw_buffer_load_b128(remote ? part_rs : none_rs, off, 0u, AUX));
             v[i][sp] = sj == split ? acc[t][r] : x;
           }
         }
@@ -414,11 +460,15 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
       }
     }
   };
-  if (p.splits <= 64)
-    combine(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
-  else
-    combine(std::integral_constant<int, 1>{}, std::integral_constant<int, 6>{});
-  if (tid == 0) __hip_atomic_store(&p.counters[tile * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (p.splits <= 64) {
+    if (local)
+      combine(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, kL2Load>{});
+    else
+      combine(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, kCoherent>{});
+  } else {
+    combine(std::integral_constant<int, 1>{}, std::integral_constant<int, 6>{}, std::integral_constant<int, kCoherent>{});
+  }
+  rearm();
 }
 
 }  // namespace

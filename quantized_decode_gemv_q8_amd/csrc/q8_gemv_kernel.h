@@ -44,6 +44,7 @@
 
 #include "q8_common.h"
 #include "q8_sum.h"
+#include "q8_xcd.h"
 
 namespace q8 {
 namespace {
@@ -465,23 +466,6 @@ __device__ __forceinline__ v4f load_partial_quad(__amdgpu_buffer_rsrc_t rs, int 
   return v4f{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
 }
 
-// Id of the XCD this wave runs on (the XCC_ID hardware register; its low
-// four bits).
-__device__ __forceinline__ uint32_t xcd_id() {
-  uint32_t x;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-  return x & 15u;
-}
-
-// The split-K counter of a tile whose runs are placed on one XCD is 64 bits:
-// the number of contributors in bits 0-14, a count of contributors that
-// report an XCD numbered 8 or above from bit 15, and a 6-bit count per XCD x
-// at bit 16 + 6x.  A contributor on XCD x adds xcd_increment(x); the last one
-// checks that every contributor counted on its own XCD.
-__device__ __forceinline__ uint64_t xcd_increment(uint32_t x) {
-  return 1ull + (x < 8 ? 1ull << (16 + 6 * x) : 1ull << 15);
-}
-
 // Workgroup that owns unit u when units are dealt in runs of upw (+1 for the
 // first rem workgroups).
 __device__ __forceinline__ int wg_of_unit(int u, int upw, int rem) {
@@ -738,8 +722,8 @@ __global__ __launch_bounds__(kThreads) void q8_gemv_kernel(GemvArgs p) {
           const uint64_t prev = __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(cnt), inc, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
           const uint64_t n = (uint64_t)(i1 - i0 + 1);
-          last = (prev & 0x7fffu) == n - 1;
-          stray = last && (x >= 8 || prev + inc != n + (n << (16 + 6 * x)));
+          last = xcd_count_done(prev, n);
+          stray = last && !xcd_all_here(prev, x, n);
         } else {
           const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           last = prev == (uint32_t)(i1 - i0);

@@ -327,7 +327,8 @@ def _with_xcd_mode(mode, fn):
             os.environ["Q8_XCD_LOCAL"] = old
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2, 8192, 8192), (1, 28672, 4096)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2, 8192, 8192), (1, 28672, 4096),
+                                   (16, 8192, 4096), (48, 4096, 4096), (8, 4096, 8192)])
 def test_xcd_local_combine_is_bitwise_the_same(M, K, N, capfd):
     """Tiles whose runs all sit on one XCD keep their split-K partials in that
     XCD's L2; the sums are the same bit for bit as with device-coherent
@@ -346,13 +347,13 @@ def test_xcd_local_combine_is_bitwise_the_same(M, K, N, capfd):
     assert np.array_equal(C_local.view(np.uint32), C_dev.view(np.uint32))
 
 
-def test_xcd_local_stray_contributors_give_nan():
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (16, 8192, 4096)])
+def test_xcd_local_stray_contributors_give_nan(M, K, N):
     """If a tile's contributors report different XCDs, the tile's outputs are
     NaN (its partials may not be readable from one L2); the counters are
-    re-armed, so the next call is correct."""
-    M, K, N = 1, 4096, 4096
-    A, W, S = rand_q8(M, K, N, 143)
-    print("[q8] xcd-local stray contributors", flush=True)
+    re-armed, so the next call is correct.  Stream path and matrix cores."""
+    A, W, S = rand_q8(M, K, N, (143, M))
+    print(f"[q8] xcd-local stray contributors M={M} K={K} N={N}", flush=True)
     C = _with_xcd_mode("stray", lambda: gpu_q8(A, W, S))
     assert np.all(np.isnan(C))
     assert_parity(A, W, S, gpu_q8(A, W, S))
