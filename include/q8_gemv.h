@@ -128,7 +128,9 @@ q8_status q8_matvec_noalloc(const float *A, const int8_t *W, const float *S, flo
  * For Q8_PLAN_MATRIX, the matrix-core product of 2..64 rows ("dot and tensor
  * cores", "Hardware paths"; A is split into three bf16 parts so that the
  * result keeps f32 accuracy; one pass over W serves all rows): it needs
- * N % 16 == 0, 16-byte aligned W and S and 4*M*K < 2^31 (A's byte offsets
+ * N % 4 == 0, 4-byte aligned W, 16-byte aligned S and 4*M*K < 2^31 (W is
+ * read in 16-, 8- or 4-byte pieces, the widest that N and W's address both
+ * allow, so a ragged last column tile is masked, "Bounds"; A's byte offsets
  * are 32-bit on this path; an explicit matrix plan beyond that returns
  * Q8_ERR_TOO_LARGE, and automatic plans use the stream), and serves
  * q8_matvec, q8_matvec_with_plan and a plain single-sibling fused call.

@@ -338,8 +338,8 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   const bool matrix_a_fits = 4 * M * K < kIndexLimit;
   // Automatic matrix plans split K into at most 64 blocks per split, and the
   // splits must fit the grid.
-  const bool matrix_shape = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 && N % 16 == 0 &&
-                            w_align % 16 == 0 && s_align % 16 == 0 &&
+  const bool matrix_shape = matrix_ok && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0 &&
+                            q8::gemm_w_width(N, w_align) != 0 && s_align % 16 == 0 &&
                             ceil_div(ceil_div(K, kBlock), 64) <= kMaxGridY;
   const bool matrix_fits = matrix_shape && matrix_a_fits;
   // Automatic choice, from timings on MI355X under graph submission.  The
@@ -374,8 +374,8 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
                   : Q8_PLAN_STREAM;
     if (pl.kind == Q8_PLAN_STREAM && M >= 2 && M <= Q8_MATRIX_MAX_ROWS && K > 0) {
       nt.matrix = !matrix_ok               ? "matrix cores serve one weight set with the plain epilogue"
-                  : N % 16 != 0            ? "matrix cores need N % 16 == 0"
-                  : w_align % 16 != 0 || s_align % 16 != 0 ? "matrix cores need 16-byte aligned W and S"
+                  : N % 4 != 0             ? "matrix cores need N % 4 == 0"
+                  : w_align % 4 != 0 || s_align % 16 != 0 ? "matrix cores need 4-byte aligned W and 16-byte aligned S"
                   : !matrix_a_fits         ? "matrix cores need A below 2^31 bytes"
                   : !matrix_shape          ? "too many K splits for the matrix-core grid"
                   : pl.vec != 0 || pl.m_tile != 0 || pl.workgroups != 0 ? "stream fields set in the plan"
@@ -565,6 +565,7 @@ q8_status fused_impl(const float *A, const q8_sibling *sib, int64_t n_sib, int64
     g.n_tiles = (int)ceil_div(N, q8::kGemmTileCols);
     g.splits = pl.workgroups / g.n_tiles;
     g.bps = (int)ceil_div(KB, g.splits);
+    g.w_width = q8::gemm_w_width(N, w_align);
     // The splits of a tile are on grid y: with a multiple of 8 tiles they all
     // run on the tile's XCD, and their partials can stay in its L2 (at most
     // 63 splits: the counter's per-XCD fields).

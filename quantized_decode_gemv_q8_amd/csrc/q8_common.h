@@ -123,7 +123,16 @@ struct GemmArgs {
   int n_tiles, splits, bps;
   int xcd_local;       // nonzero: every split of a tile runs on one XCD (n_tiles a multiple of 8); partials stay in its L2
   int xcc_skew;        // testing only: nonzero makes some splits report another XCD
+  int w_width;         // bytes per W load: 16, 8 or 4 (N and W's address are multiples of it)
 };
+
+// Widest W load of the matrix-core product that N and W's address allow (16,
+// 8 or 4 bytes), or 0 if W rows are not 4-byte aligned.
+constexpr int gemm_w_width(int64_t N, int64_t w_align) {
+  return N % 16 == 0 && w_align % 16 == 0 ? 16 : N % 8 == 0 && w_align % 8 == 0 ? 8
+         : N % 4 == 0 && w_align % 4 == 0                                      ? 4
+                                                                               : 0;
+}
 
 // Rows of A the matrix-core product takes at most, its column tile and its
 // waves per workgroup.

@@ -24,9 +24,12 @@
 //     contiguous range of K blocks (a split); the splits of a tile are
 //     combined as in the matvec: device-coherent partials, an arrival
 //     counter, and the last arrival sums the splits in K order.
-//   * Per block the workgroup loads W[32 rows, 512 columns] with 16-byte
-//     loads (a wave instruction reads two whole 512-byte row segments) into
-//     LDS, two blocks ahead in registers.  A's block (M x 32) is split into
+//   * Per block the workgroup loads W[32 rows, 512 columns] into LDS, two
+//     blocks ahead in registers, with 16-byte loads (a wave instruction reads
+//     two whole 512-byte row segments).  When N or W's address is not a
+//     multiple of 16 ("Bounds": N need not fill the tiles) the loads are 8
+//     bytes (one 512-byte row segment per instruction) or 4 bytes (half a
+//     segment), whichever both allow.  A's block (M x 32) is split into
 //     its three bf16 parts in LDS once per workgroup.
 //   * Wave w computes columns [64w, 64w + 64) as four 16x16 output tiles per
 //     16 rows of A.  For the B operand a lane needs eight consecutive k of one
@@ -50,6 +53,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGemmCols = kGemmTileCols;   // columns per workgroup tile
 constexpr int kGW = kGemmWaves;            // waves per workgroup
@@ -57,7 +61,6 @@ constexpr int kGThreads = 64 * kGW;
 constexpr int kWaveCols = kGemmCols / kGW; // columns per wave (64)
 constexpr int kWaveTiles = kWaveCols / 16; // 16-column output tiles per wave
 constexpr int kWaveGroups = kWaveCols / 64;  // groups of 64 columns per wave
-constexpr int kRowPairs = kBlock / (2 * kGW);  // W row pairs per wave and block
 constexpr int kWPitch = kGemmCols + 16;    // LDS row pitch of a W block, bytes (16-byte aligned rows)
 constexpr int kAPitch = 40;                // LDS row pitch of an A block part, bf16 (80 bytes)
 constexpr int kDepthG = 2;                 // W blocks held in registers ahead of the one in LDS
@@ -103,8 +106,21 @@ struct SFor {
 };
 
 // RT: 16-row tiles of A (M <= 16 * RT).
-template <int RT>
+// WW: bytes per W load (16, 8 or 4); N and W's address are multiples of it.
+template <int RT, int WW>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 : 2))) void q8_gemm_kernel(GemmArgs p) {
+  static_assert(WW == 16 || WW == 8 || WW == 4, "16-, 8- or 4-byte W loads");
+  using WVec = std::conditional_t<WW == 16, u4, std::conditional_t<WW == 8, u2, uint32_t>>;
+  // A tile row of W is kGemmCols / WW lanes' pieces.  One load instruction of
+  // a wave covers kRowsPerLoad rows (two for 16-byte loads) or 64 lanes'
+  // pieces of one row; kSides loads cover a row side by side (two for 4-byte
+  // loads).  kWLoads loads per lane bring in the wave's rows of a block.
+  constexpr int kLanesPerRow = kGemmCols / WW;
+  constexpr int kPieceLanes = kLanesPerRow < 64 ? kLanesPerRow : 64;
+  constexpr int kSides = kLanesPerRow / kPieceLanes;
+  constexpr int kRowsPerLoad = 64 / kPieceLanes;
+  constexpr int kWaveRows = kBlock / kGW;  // rows of a block per wave
+  constexpr int kWLoads = kWaveRows * kSides / kRowsPerLoad;
   // Two LDS buffers: block j is staged in buffer j & 1, so staging the next
   // block never overwrites the one other waves may still be reading, and one
   // barrier per block suffices.
@@ -142,22 +158,35 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   const uint32_t s_bytes = (uint32_t)p.KB * (uint32_t)p.N * 4u;
   const uint32_t a_bytes = (uint32_t)p.M * (uint32_t)p.K * 4u;
 
-  // This thread's 16-byte piece of a W block: row (32/kGW)*wave + 2*i +
-  // lane/32, columns n0 + 16*(lane%32) .. +15, for i < kRowPairs.  The row pair's first
-  // row goes into the wave-uniform scalar offset, clamped to K - 1; the
-  // second is a per-lane step of one row, taken only while that row exists.
-  // Columns past N (the ragged last tile; N is a multiple of 16) read column
-  // 0, rows past K re-read a row of W; their activations are zero.
-  const int wcol = n0 + 16 * (lane & 31);
-  const uint32_t w_voff = wcol < p.N ? (uint32_t)wcol : 0u;
-  const bool upper = (lane >> 5) != 0;
-  auto load_w = [&](int b, bool live, u4 (&x)[kRowPairs]) {
+  // This thread's WW-byte piece of a W block in load i: row kWaveRows*wave
+  // + kRowsPerLoad*(i/kSides) + lrow of the block, columns n0 + w_col(i % kSides)
+  // .. +WW-1.  The load's first row goes into the wave-uniform scalar offset,
+  // clamped to K - 1; with 16-byte loads the upper half-wave steps one row
+  // further per lane, only while that row exists.  Columns past N (the
+  // ragged last tile; N is a multiple of WW) read column 0, rows past K
+  // re-read a row of W; their activations are zero, and outputs past N are
+  // not stored.
+  const int lrow = lane / kPieceLanes;  // 0, or 1 for the upper half-wave of 16-byte loads
+  auto w_col = [&](int side) { return WW * (kPieceLanes * side + lane % kPieceLanes); };
+  uint32_t w_voff[kSides];
+#pragma unroll
+  for (int v = 0; v < kSides; ++v) {
+    const int wcol = n0 + w_col(v);
+    w_voff[v] = wcol < p.N ? (uint32_t)wcol : 0u;
+  }
+  auto load_w = [&](int b, bool live, WVec (&x)[kWLoads]) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(p.W, live ? w_bytes : 0u);
 #pragma unroll
-    for (int i = 0; i < kRowPairs; ++i) {
-      const int r = min(b * kBlock + (kBlock / kGW) * wave + 2 * i, p.K - 1);
-      const uint32_t voff = w_voff + (upper && r + 1 < p.K ? (uint32_t)p.N : 0u);
-      x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (uint32_t)r * (uint32_t)p.N, kStreamPolicyG);
+    for (int i = 0; i < kWLoads; ++i) {
+      const int r = min(b * kBlock + kWaveRows * wave + kRowsPerLoad * (i / kSides), p.K - 1);
+      const uint32_t voff = w_voff[i % kSides] + (lrow != 0 && r + 1 < p.K ? (uint32_t)p.N : 0u);
+      const uint32_t soff = (uint32_t)r * (uint32_t)p.N;
+      if constexpr (WW == 16)
+        x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kStreamPolicyG);
+      else if constexpr (WW == 8)
+        x[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kStreamPolicyG);
+      else
+        x[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kStreamPolicyG);
     }
   };
 
@@ -204,7 +233,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   };
 
   // Register ring: W, A and S of blocks b_begin + j for j < kDepthG are in flight.
-  u4 wring[kDepthG][kRowPairs];
+  WVec wring[kDepthG][kWLoads];
   float aring[kDepthG][kAElems];
   u4 sring[kDepthG][kWaveGroups];
 #pragma unroll
@@ -226,9 +255,9 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
       int8_t *w_lds = w_lds_buf[j & 1];
       uint16_t(*a_lds)[16 * RT * kAPitch] = a_lds_buf[j & 1];
 #pragma unroll
-      for (int i = 0; i < kRowPairs; ++i) {
-        const int row = (kBlock / kGW) * wave + 2 * i + (lane >> 5);
-        *reinterpret_cast<u4 *>(&w_lds[row * kWPitch + 16 * (lane & 31)]) = wring[D][i];
+      for (int i = 0; i < kWLoads; ++i) {
+        const int row = kWaveRows * wave + kRowsPerLoad * (i / kSides) + lrow;
+        *reinterpret_cast<WVec *>(&w_lds[row * kWPitch + w_col(i % kSides)]) = wring[D][i];
       }
 #pragma unroll
       for (int jj = 0; jj < kAElems; ++jj) {
@@ -476,14 +505,24 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
   if (a.M < 1 || a.M > kGemmMaxRows) return hipErrorInvalidValue;
   const int rt = gemm_row_tiles(a.M);
+  if (a.w_width != 16 && a.w_width != 8 && a.w_width != 4) return hipErrorInvalidValue;
+  if (a.N % a.w_width != 0 || (reinterpret_cast<uintptr_t>(a.W) % a.w_width) != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)a.n_tiles, (unsigned)a.splits, (unsigned)((a.M + 16 * rt - 1) / (16 * rt)));
-  if (rt == 1) {
-    hipLaunchKernelGGL(q8_gemm_kernel<1>, grid, dim3(kGThreads), 0, stream, a);
-  } else if (rt == 2) {
-    hipLaunchKernelGGL(q8_gemm_kernel<2>, grid, dim3(kGThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(q8_gemm_kernel<4>, grid, dim3(kGThreads), 0, stream, a);
-  }
+  auto go = [&](auto rt_) {
+    constexpr int R = decltype(rt_)::value;
+    if (a.w_width == 16)
+      hipLaunchKernelGGL((q8_gemm_kernel<R, 16>), grid, dim3(kGThreads), 0, stream, a);
+    else if (a.w_width == 8)
+      hipLaunchKernelGGL((q8_gemm_kernel<R, 8>), grid, dim3(kGThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((q8_gemm_kernel<R, 4>), grid, dim3(kGThreads), 0, stream, a);
+  };
+  if (rt == 1)
+    go(std::integral_constant<int, 1>{});
+  else if (rt == 2)
+    go(std::integral_constant<int, 2>{});
+  else
+    go(std::integral_constant<int, 4>{});
   return hipGetLastError();
 }
 

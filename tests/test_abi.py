@@ -54,8 +54,8 @@ def test_plan_is_valid_and_normalised(M, K, N):
     p = plan(M, K, N)
     KB = math.ceil(K / 32)
     if p["kind"] == binding.PLAN_MATRIX:
-        # matrix cores: 2..64 rows, N a multiple of 16, 512-column tiles x K splits, 8 waves
-        assert 2 <= M <= 64 and N % 16 == 0 and p["vec"] == 0 and p["m_tile"] == 0 and p["waves"] == 8
+        # matrix cores: 2..64 rows, N a multiple of 4, 512-column tiles x K splits, 8 waves
+        assert 2 <= M <= 64 and N % 4 == 0 and p["vec"] == 0 and p["m_tile"] == 0 and p["waves"] == 8
         tiles = math.ceil(N / 512)
         assert p["workgroups"] % tiles == 0
         splits = p["workgroups"] // tiles
@@ -75,13 +75,13 @@ def test_plan_vec_follows_shape_and_alignment():
     assert plan(1, 8192, 28672)["vec"] == 8     # automatic plans use at most 8-byte lanes
     assert plan(1, 4096, 4096)["vec"] == 4      # under 2 units per CU at vec 8: 4-byte lanes
     assert plan(1, 4096, 4096, cus=64)["vec"] == 8
-    assert plan(4, 4100, 5000)["vec"] == 4      # 4 rows on the stream (N % 16 != 0): vec * m_tile <= 16
-    assert plan(2, 8192, 28680)["vec"] == 8     # 2 rows on the stream (N % 16 != 0): 2 * 8 <= 16
+    assert plan(4, 4100, 5000)["vec"] == 4      # 4 rows on the stream (K*N < 2^25): vec * m_tile <= 16
+    assert plan(2, 12288, 8200)["vec"] == 8     # 2 rows on the stream (K*N < 2^27): 2 * 8 <= 16
     assert plan(1, 64, 4100)["vec"] == 4
     assert plan(1, 64, 4096, w_align=4)["vec"] == 4
     assert plan(1, 64, 4096, s_align=8)["vec"] == 2
     assert plan(1, 64, 7)["vec"] == 1
-    assert plan(8, 64, 4100)["vec"] == 2        # 8 rows on the stream (N % 16 != 0): 8 * vec <= 16
+    assert plan(8, 64, 4100)["vec"] == 2        # 8 rows on the stream (a small W): 8 * vec <= 16
     assert plan(2, 64, 4104)["m_tile"] == 2
 
 
@@ -93,8 +93,14 @@ def test_plan_kind_follows_rows_and_layout():
     assert plan(33, 8192, 28672)["kind"] == binding.PLAN_MATRIX    # the 64-row instance
     assert plan(64, 8192, 28672)["kind"] == binding.PLAN_MATRIX
     assert plan(65, 8192, 28672)["kind"] == binding.PLAN_STREAM    # above it
-    assert plan(16, 8192, 5000)["kind"] == binding.PLAN_STREAM     # N % 16 != 0
-    assert plan(16, 8192, 4096, w_align=8)["kind"] == binding.PLAN_STREAM
+    # ragged N: the matrix cores read W in 8- or 4-byte pieces, as long as
+    # W rows are 4-byte aligned and S rows 16-byte aligned
+    assert plan(16, 8192, 5000)["kind"] == binding.PLAN_MATRIX     # N % 8 == 0
+    assert plan(16, 8192, 5004)["kind"] == binding.PLAN_MATRIX     # N % 4 == 0
+    assert plan(16, 8192, 4096, w_align=4)["kind"] == binding.PLAN_MATRIX
+    assert plan(16, 8192, 5002)["kind"] == binding.PLAN_STREAM     # N % 4 != 0
+    assert plan(16, 8192, 4096, w_align=2)["kind"] == binding.PLAN_STREAM
+    assert plan(16, 8192, 4096, s_align=8)["kind"] == binding.PLAN_STREAM
     # up to 4 rows of a small W stay on the stream; 5 rows or a large W go to the matrix cores
     assert plan(4, 4096, 4096)["kind"] == binding.PLAN_STREAM
     assert plan(2, 4096, 4096)["kind"] == binding.PLAN_STREAM

@@ -184,9 +184,13 @@ def test_matrix_invalid_plans():
     A65, W65, S65 = (to_dev(x) for x in workloads.q8_inputs(65, 256, 1024, 314))
     with pytest.raises(binding.Q8Error):
         binding.q8_matvec_with_plan(A65, W65, S65, MATRIX)  # above 64 rows
-    A2, W2, S2 = (to_dev(x) for x in workloads.q8_inputs(16, 256, 1000, 310))
+    A2, W2, S2 = (to_dev(x) for x in workloads.q8_inputs(16, 256, 1002, 310))
     with pytest.raises(binding.Q8Error):
-        binding.q8_matvec_with_plan(A2, W2, S2, MATRIX)  # N % 16 != 0
+        binding.q8_matvec_with_plan(A2, W2, S2, MATRIX)  # N % 4 != 0: W rows not 4-byte aligned
+    Wbuf = torch.empty(256 * 1024 + 16, dtype=torch.int8, device=DEV)
+    W3 = Wbuf[2:2 + 256 * 1024].view(256, 1024)
+    with pytest.raises(binding.Q8Error):
+        binding.q8_matvec_with_plan(A, W3, S, MATRIX)  # W's address not 4-byte aligned
 
 
 @pytest.mark.parametrize("M", [17, 45])
@@ -203,3 +207,40 @@ def test_matrix_canaries(M):
     host = buf.cpu().numpy()
     assert np.all(host[:pad] == 1.0) and np.all(host[-pad:] == -2.0)
     assert_parity(A, W, S, out.cpu().numpy())
+
+
+# "Bounds": N need not fill the 512-column tiles nor be a multiple of 16.  W
+# is then read in 8- or 4-byte pieces (the widest that N and W's address
+# allow), and the columns past N in the last tile are not stored.
+@pytest.mark.parametrize("M", [2, 4, 16, 24, 64])
+@pytest.mark.parametrize("K,N", [(4100, 5000), (1000, 1000), (96, 516), (64, 4), (4100, 1028), (300, 2056)])
+def test_matrix_ragged_n(M, K, N):
+    A, W, S = workloads.q8_inputs(M, K, N, (330, M, K, N))
+    print(f"[gemm] ragged N: M={M} K={K} N={N}", flush=True)
+    assert_parity(A, W, S, gpu_q8(A, W, S, MATRIX))
+
+
+def w_at_offset(W, off):
+    """A device copy of W whose address is `off` bytes past a 256-byte boundary."""
+    K, N = W.shape
+    buf = torch.zeros(K * N + 256, dtype=torch.int8, device=DEV)
+    view = buf[off:off + K * N].view(K, N)
+    view.copy_(torch.from_numpy(np.ascontiguousarray(W)).to(DEV))
+    assert view.data_ptr() % 16 == off % 16
+    return view
+
+
+# The load width changes which lanes bring in which bytes, not the sums: the
+# results are bitwise the same for 16-, 8- and 4-byte loads.
+@pytest.mark.parametrize("M,K,N", [(16, 4100, 4096), (64, 1000, 1536), (3, 8192, 2048), (32, 256, 512)])
+def test_matrix_load_widths_agree(M, K, N):
+    A, W, S = workloads.q8_inputs(M, K, N, (331, M, K, N))
+    A_d, S_d = to_dev(A), to_dev(S)
+    outs = []
+    for off in (0, 8, 4):
+        print(f"[gemm] W offset {off}: M={M} K={K} N={N}", flush=True)
+        C = binding.q8_matvec_with_plan(A_d, w_at_offset(W, off), S_d, MATRIX)
+        torch.cuda.synchronize()
+        outs.append(C.cpu().numpy())
+    assert_parity(A, W, S, outs[0])
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])

@@ -46,7 +46,7 @@ def test_plan_log_names_paths_and_fallbacks(monkeypatch, capfd):
     assert len(xcd) == 1 and "16 tiles" in xcd[0], xcd
     assert len(lines) == 4, lines
     assert "matvec M=4 K=4100 N=5000" in lines[0] and "stream" in lines[0]
-    assert "not on the matrix cores: matrix cores need N % 16 == 0" in lines[0]
+    assert "not on the matrix cores: too few rows or too small a W" in lines[0]
     assert "matvec M=16 K=4096 N=8192" in lines[1] and "matrix cores" in lines[1]
     assert "dot_t M=4 K=256 N=64: sdot4" in lines[2] and "M < 16" in lines[2]
     assert "dot_t_f32 M=33 K=30 N=40" in lines[3] and "4-byte loads: K % 4 != 0" in lines[3]
