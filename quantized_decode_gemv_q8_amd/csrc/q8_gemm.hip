@@ -70,12 +70,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Round-to-nearest-even f32 -> bf16 bits (finite inputs).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even bf16 of (x, y) packed into one dword, x in the low
+// half (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, y}, bf16x2));
 }
-__device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Two signed bytes (byte `i` of words x0 and x1) as a pair of bf16 in one
 // dword, x0's in the low half.  Exact: the f32 of a byte has 16 zero low bits.
@@ -201,22 +203,37 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
     s_voff[q] = c < p.N ? (uint32_t)c * 4u : 0u;
   }
 
-  // Activation block b: elements e = tid + 256 j of the 16*RT x 32 block.
-  constexpr int kAElems = 16 * RT * kBlock / kGThreads;  // per thread
-  // Elements past M or K load element 0; they are replaced by zero when the
-  // block is staged (not here, which would wait for the load at once).
-  auto a_ok = [&](int b, int j) {
-    const int e = tid + kGThreads * j;
-    return (e >> 5) < p.M && b * kBlock + (e & 31) < p.K;
-  };
+  // Activation block b: pairs of adjacent k, pair i = tid + kGThreads * j of
+  // the 16*RT x 32 block (16 pairs per row), so that one convert rounds two
+  // elements.  With 16 rows there are 256 pairs: waves 4-7 stage none.
+  constexpr int kAPairs = (16 * RT * kBlock / 2 + kGThreads - 1) / kGThreads;  // per thread
+  constexpr int kAElems = 2 * kAPairs;
+  const bool a_stager = 16 * RT * kBlock / 2 >= kGThreads || tid < 16 * RT * kBlock / 2;
+  // Element h of pair j: row i/16, k = 2 (i % 16) + h.  Elements past M or K
+  // load element 0; they are replaced by zero when the block is staged (not
+  // here, which would wait for the load at once).  The row test and the row's
+  // offset are fixed for the whole loop; the tests combine with & so that
+  // they stay selects (a short-circuit test became branches around the loads).
+  bool a_row_ok[kAPairs];
+  int a_kk[kAPairs];
+  uint32_t a_row_off[kAPairs];
+#pragma unroll
+  for (int j = 0; j < kAPairs; ++j) {
+    const int i = tid + kGThreads * j;
+    a_row_ok[j] = a_stager & ((i >> 4) < p.M);
+    a_kk[j] = 2 * (i & 15);
+    a_row_off[j] = (uint32_t)(i >> 4) * (uint32_t)p.K + (uint32_t)a_kk[j];
+  }
+  auto a_ok = [&](int b, int j, int h) { return a_row_ok[j] & (b * kBlock + a_kk[j] + h < p.K); };
   auto load_a = [&](int b, bool live, float (&v)[kAElems]) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(p.A, live ? a_bytes : 0u);
 #pragma unroll
-    for (int j = 0; j < kAElems; ++j) {
-      const int e = tid + kGThreads * j;
-      const uint32_t off = a_ok(b, j) ? ((uint32_t)(e >> 5) * (uint32_t)p.K + (uint32_t)(b * kBlock + (e & 31))) * 4u : 0u;
-      v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0u, 0));
-    }
+    for (int j = 0; j < kAPairs; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t off = a_ok(b, j, h) ? (a_row_off[j] + (uint32_t)(b * kBlock + h)) * 4u : 0u;
+        v[2 * j + h] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0u, 0));
+      }
   };
 
   f4 acc[kWaveTiles][RT];
@@ -259,19 +276,26 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
         const int row = kWaveRows * wave + kRowsPerLoad * (i / kSides) + lrow;
         *reinterpret_cast<WVec *>(&w_lds[row * kWPitch + w_col(i % kSides)]) = wring[D][i];
       }
+      // A's three parts: each part is the rounding of what the parts before
+      // left, and each remainder is exact in f32.
+      if (a_stager) {
 #pragma unroll
-      for (int jj = 0; jj < kAElems; ++jj) {
-        const int e = tid + kGThreads * jj;
-        const int m = e >> 5;
-        const int k = e & 31;
-        const float a = a_ok(b, jj) ? aring[D][jj] : 0.f;
-        const uint32_t hi = bf16_bits(a);
-        const float r1 = a - bf16_value(hi);
-        const uint32_t mid = bf16_bits(r1);
-        const float r2 = r1 - bf16_value(mid);
-        a_lds[0][m * kAPitch + k] = (uint16_t)hi;
-        a_lds[1][m * kAPitch + k] = (uint16_t)mid;
-        a_lds[2][m * kAPitch + k] = (uint16_t)bf16_bits(r2);
+        for (int jj = 0; jj < kAPairs; ++jj) {
+          const int i = tid + kGThreads * jj;
+          const int m = i >> 4;
+          const int k = 2 * (i & 15);
+          float x = a_ok(b, jj, 0) ? aring[D][2 * jj] : 0.f;
+          float y = a_ok(b, jj, 1) ? aring[D][2 * jj + 1] : 0.f;
+#pragma unroll
+          for (int q = 0; q < 3; ++q) {
+            const uint32_t u = pk_bf16(x, y);
+            *reinterpret_cast<uint32_t *>(&a_lds[q][m * kAPitch + k]) = u;
+            if (q < 2) {
+              x -= __uint_as_float(u << 16);
+              y -= __uint_as_float(u & 0xffff0000u);
+            }
+          }
+        }
       }
       lds_barrier();
       // Refill this ring slot with block j + kDepthG (past the split's end:
