@@ -62,7 +62,11 @@ constexpr int kWaveCols = kGemmCols / kGW; // columns per wave (64)
 constexpr int kWaveTiles = kWaveCols / 16; // 16-column output tiles per wave
 constexpr int kWaveGroups = kWaveCols / 64;  // groups of 64 columns per wave
 constexpr int kWPitch = kGemmCols + 16;    // LDS row pitch of a W block, bytes (16-byte aligned rows)
-constexpr int kAPitch = 40;                // LDS row pitch of an A block part, bf16 (80 bytes)
+// LDS row pitch of an A block part, bf16 (96 bytes).  Measured with
+// SQ_LDS_BANK_CONFLICT at 64 rows: 8.7 M conflict cycles per launch at 80
+// bytes, 112 and 144 bytes, 3.2 M at 96 bytes (the pitch the dense kernels'
+// part tiles also use).
+constexpr int kAPitch = 48;
 constexpr int kDepthG = 2;                 // W blocks held in registers ahead of the one in LDS
 constexpr int kStreamPolicyG = 2;          // non-temporal: W and S are read once
 
