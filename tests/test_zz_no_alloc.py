@@ -44,6 +44,7 @@ def run_pair(M, K, N, seed):
     ((1, 8192, 28672), (1, 4100, 5000)),    # split-K stream: the headline shape, then a ragged smaller one
     ((4, 4100, 5000), (2, 1000, 300)),      # several rows per pass, then a short K
     ((16, 4096, 8192), (8, 1000, 1024)),    # matrix-core product, then a smaller one
+    ((16, 8192, 5000), (24, 1000, 1000)),   # matrix cores with ragged N (8-byte W loads), then a smaller one
 ])
 def test_noalloc_matches_q8_matvec_on_consecutive_calls(first, second):
     print(f"[no_alloc] {first} then {second}", flush=True)
