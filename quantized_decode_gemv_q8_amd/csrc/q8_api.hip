@@ -351,7 +351,11 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   //     half the CUs (K = 4096, N = 14336: 21.2 against 32.7 us), not on a
   //     narrow W (K = 14336, N = 4096, 64 workgroups: 44.3 against 35.1).
   //   * At 2 rows they win only from K*N >= 2^27 (K = 8192, N = 28672: 50.0
-  //     against 55.9 us; K = N = 8192: 28.4 against 21.7).
+  //     against 55.9 us; K = N = 8192: 28.4 against 21.7), and only with
+  //     16-byte W loads (K = 8192, N = 28680, 8-byte loads: 62.0 against
+  //     55.3 us).  From 3 rows the narrower loads still win: K = 8192,
+  //     N = 12296 at 3 rows 33.3 against 54.9 us, N = 12292 (4-byte loads)
+  //     at 4 rows 35.6 against 55.0.
   const int64_t gemm_wgs =
       K > 0 && N > 0 ? ceil_div(N, q8::kGemmTileCols) * gemm_auto_splits(M, K, N, num_cus) : 0;
   const bool gemm_fills = 2 * gemm_wgs >= (int64_t)num_cus;     // half the CUs
@@ -366,7 +370,7 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   //     64 workgroups: 20.5 against 15.4; K = 14336, N = 1024, 112: a tie.
   const bool matrix_pays = (M > 16) || (M >= 9 && gemm_quarter) || (M >= 5 && gemm_3_8ths) ||
                            (M >= 3 && K * N >= ((int64_t)1 << 25) && gemm_fills) ||
-                           (M == 2 && K * N >= ((int64_t)1 << 27) && gemm_fills);
+                           (M == 2 && K * N >= ((int64_t)1 << 27) && gemm_fills && q8::gemm_w_width(N, w_align) == 16);
   if (pl.kind == 0) {
     pl.kind = (matrix_fits && matrix_pays && M >= Q8_MATRIX_MIN_ROWS && pl.vec == 0 && pl.m_tile == 0 &&
                pl.workgroups == 0)

@@ -101,6 +101,11 @@ def test_plan_kind_follows_rows_and_layout():
     assert plan(16, 8192, 5002)["kind"] == binding.PLAN_STREAM     # N % 4 != 0
     assert plan(16, 8192, 4096, w_align=2)["kind"] == binding.PLAN_STREAM
     assert plan(16, 8192, 4096, s_align=8)["kind"] == binding.PLAN_STREAM
+    # at 2 rows the matrix cores pay only with 16-byte W loads
+    assert plan(2, 8192, 28672)["kind"] == binding.PLAN_MATRIX
+    assert plan(2, 8192, 28680)["kind"] == binding.PLAN_STREAM     # N % 16 == 8
+    assert plan(2, 8192, 28672, w_align=8)["kind"] == binding.PLAN_STREAM
+    assert plan(3, 8192, 12296)["kind"] == binding.PLAN_MATRIX     # from 3 rows 8-byte loads still pay
     # up to 4 rows of a small W stay on the stream; 5 rows or a large W go to the matrix cores
     assert plan(4, 4096, 4096)["kind"] == binding.PLAN_STREAM
     assert plan(2, 4096, 4096)["kind"] == binding.PLAN_STREAM
