@@ -47,7 +47,7 @@ def draw_stream_case(i):
 def draw_matrix_case(i):
     rng = np.random.default_rng((701, i))
     M = int(rng.integers(2, 65))
-    N = 16 * int(rng.integers(1, 201))
+    N = 4 * int(rng.integers(1, 801))  # any N % 4 == 0: 16-, 8- and 4-byte W loads
     K = int(rng.integers(1, 5001))
     KB = math.ceil(K / 32)
     s = int(rng.integers(1, min(KB, 80) + 1))
