@@ -352,10 +352,10 @@ q8_status resolve_plan(int64_t M, int64_t K, int64_t N, int64_t n_sib, int64_t w
   //     narrow W (K = 14336, N = 4096, 64 workgroups: 44.3 against 35.1).
   //   * At 2 rows they win only from K*N >= 2^27 (K = 8192, N = 28672: 50.0
   //     against 55.9 us; K = N = 8192: 28.4 against 21.7), and only with
-  //     16-byte W loads (K = 8192, N = 28680, 8-byte loads: 62.0 against
-  //     55.3 us).  From 3 rows the narrower loads still win: K = 8192,
-  //     N = 12296 at 3 rows 33.3 against 54.9 us, N = 12292 (4-byte loads)
-  //     at 4 rows 35.6 against 55.0.
+  //     16-byte W loads (K = 8192, N = 28680, 8-byte loads: 59.1 against
+  //     54.4 us; N = 28672: 49.1 against 52.7).  From 3 rows the narrower
+  //     loads still win: K = 8192, N = 12296 at 3 rows 31.4 against 54.8 us,
+  //     N = 12292 (4-byte loads) at 4 rows 32.3 against 54.9.
   const int64_t gemm_wgs =
       K > 0 && N > 0 ? ceil_div(N, q8::kGemmTileCols) * gemm_auto_splits(M, K, N, num_cus) : 0;
   const bool gemm_fills = 2 * gemm_wgs >= (int64_t)num_cus;     // half the CUs
