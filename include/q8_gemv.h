@@ -137,7 +137,8 @@ q8_status q8_matvec_noalloc(const float *A, const int8_t *W, const float *S, flo
  *   vec, m_tile  must be 0.
  *   workgroups   tiles of 512 columns times K splits (a multiple of the tile
  *           count; every split gets at least one 32-row block; at most 65535
- *           splits), or 0.
+ *           splits, and one tile's split partials, splits x rows x 2 KiB with
+ *           rows rounded up to 16, 32 or 64, below 2 GiB), or 0.
  *   waves   8 or 0 (eight waves per workgroup, 64 columns each).
  */
 #define Q8_PLAN_STREAM 1

@@ -312,6 +312,10 @@ bool finish_gemm_plan(int64_t M, int64_t K, int64_t N, int32_t num_cus, q8_plan 
   if (splits > kMaxGridY) return false;  // the splits are the grid's second dimension
   const int64_t rows = 16 * q8::gemm_row_tiles(M) * ceil_div(M, 16 * q8::gemm_row_tiles(M));  // over all passes
   if (n_tiles * splits * rows * q8::kGemmTileCols >= kIndexLimit) return false;
+  // One tile's partials are addressed with 32-bit byte offsets (the combine's
+  // buffer descriptor, and offsets pushed past it for rows beyond M), so they
+  // must stay below 2^31 bytes.  Automatic plans take at most 256 splits.
+  if (splits * rows * q8::kGemmTileCols * 4 >= kIndexLimit) return false;
   pl->workgroups = (int32_t)(n_tiles * splits);
   pl->waves = q8::kGemmWaves;
   return true;

@@ -408,6 +408,12 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
   constexpr int kCoherent = 16;  // cache policy: sc1, written through to the device's coherence point
   constexpr int kL2Load = 1;     // sc0: past the CU's L1, from the XCD's L2
   const bool local = p.xcd_local != 0;
+  // A lane's four rows of row tile r are 16r + 4(l/16) .. +3.  When they all
+  // lie past M (few rows: their partials are zero and never stored), the
+  // lane's partial store and load take an offset past the descriptor's
+  // records, so they move no data, without a branch; the rows that exist
+  // are published and summed as before.
+  auto past_m = [&](int r) { return 16 * r + 4 * g4 < p.M ? 0u : 0x80000000u; };
   const __amdgpu_buffer_rsrc_t part_rs =
       rsrc(p.partial + (size_t)tile * p.splits * kTileElems, (uint32_t)p.splits * kTileElems * 4u);
 #pragma unroll
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
     for (int r = 0; r < RT; ++r) {
       const uint32_t piece = (uint32_t)(((wave * kWaveTiles + t) * RT + r) * 64 + lane);
       const u4 v = __builtin_bit_cast(u4, acc[t][r]);
-      const uint32_t off = ((uint32_t)split * kPieces + piece) * 16u;
+      const uint32_t off = ((uint32_t)split * kPieces + piece) * 16u + past_m(r);
       if (local)
         __builtin_amdgcn_raw_buffer_store_b128(v, part_rs, off, 0u, 0);
       else
@@ -491,7 +497,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(RT ==
           for (int sp = 0; sp < 8; ++sp) {
             const int sj = c + sp;
             const bool remote = sj < p.splits && sj != split;
-            const uint32_t off = ((uint32_t)min(sj, p.splits - 1) * kPieces + piece) * 16u;
+            const uint32_t off = ((uint32_t)min(sj, p.splits - 1) * kPieces + piece) * 16u + past_m(r);
             const f4 x = __builtin_bit_cast(
                 f4, __builtin_amdgcn_raw_buffer_load_b128(remote ? part_rs : none_rs, off, 0u, AUX));
             v[i][sp] = sj == split ? acc[t][r] : x;

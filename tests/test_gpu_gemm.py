@@ -181,6 +181,13 @@ def test_matrix_invalid_plans():
     A1, W1, S1 = (to_dev(x) for x in workloads.q8_inputs(1, 256, 1024, 309))
     with pytest.raises(binding.Q8Error):
         binding.q8_matvec_with_plan(A1, W1, S1, MATRIX)  # one row
+    # one tile's split partials must stay below 2 GiB of 32-bit offsets:
+    # 64 rows x 512 columns x 4 B x 16384 splits is 2 GiB
+    Abig = torch.zeros((40, 16384 * 32), dtype=torch.float32, device=DEV)
+    Wbig = torch.zeros((16384 * 32, 16), dtype=torch.int8, device=DEV)
+    Sbig = torch.zeros((16384, 16), dtype=torch.float32, device=DEV)
+    with pytest.raises(binding.Q8Error):
+        binding.q8_matvec_with_plan(Abig, Wbig, Sbig, {"kind": binding.PLAN_MATRIX, "workgroups": 16384})
     A65, W65, S65 = (to_dev(x) for x in workloads.q8_inputs(65, 256, 1024, 314))
     with pytest.raises(binding.Q8Error):
         binding.q8_matvec_with_plan(A65, W65, S65, MATRIX)  # above 64 rows
