@@ -26,11 +26,14 @@ call per step; it matters only for kernels shorter than a Python call.
 `value` in TFLOP/s of f32 products; their `roofline` is the bf16 matrix-core
 issue rate the exact three-part split runs at (six bf16 part products per f32
 product) against the bf16 peak, and `f32_equivalent` gives the f32 view.
+Workloads on the matrix-core Q8_0 product (2-64 rows) add `bf16_mfma_issue`:
+the bf16 MFMA work that product issues against the bf16 peak.
 """
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -223,6 +226,15 @@ def device_memory_info(dev_index):
         return None
     return {"memory_clock_khz": clock.value, "bus_width_bits": width.value,
             "implied_peak_gbs": round(clock.value * 1e3 * 4 * width.value / 8 / 1e9, 1)}
+
+
+def matrix_mfma_flops(M, K, N):
+    """bf16 MFMA flops one launch of the matrix-core product issues: 2 x rows x
+    K x N for each of A's three parts, with rows padded to the instance's 16,
+    32 or 64 (per pass), K to whole 32-row blocks and N to 512-column tiles."""
+    rt = 1 if M <= 16 else 2 if M <= 32 else 4
+    rows = 16 * rt * math.ceil(M / (16 * rt))
+    return 6 * rows * math.ceil(K / 32) * 32 * math.ceil(N / 512) * 512
 
 
 def cpu_baseline(wl, A, W, S, budget_s=12.0):
@@ -577,6 +589,14 @@ def main():
                         **(device_memory_info(dev.index or 0) or {})}
     if unfused is not None:
         result["unfused"] = unfused
+    if wl.op == "q8" and used_plan.get("kind") == binding.PLAN_MATRIX:
+        # The matrix-core product's own ceiling: the bf16 MFMA work it issues
+        # (three parts of A per block; rows padded to the 16-, 32- or 64-row
+        # instance and columns to 512-wide tiles) against the bf16 peak.
+        flops = matrix_mfma_flops(wl.M, wl.K, wl.N)
+        issue = flops / launch_s / 1e12
+        result["bf16_mfma_issue"] = {"achieved": round(issue, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(issue / BF16_MFMA_PEAK_TFLOPS, 4), "flops_per_launch": flops}
     if dense:
         # The same launches counted as f32 products: against the f32 matrix
         # peak, and against the ceiling of the bf16 split (bf16 peak / 6).
